@@ -1,0 +1,97 @@
+"""Seeded synthetic inputs for the bidirectional selective scan.
+
+This module draws random numbers and rounds them to the I/O dtype; it performs none of the
+scan's own arithmetic. Both the HIP path's tests/bench and the float64 oracle take their inputs
+from here, so it imports nothing else from this package or from the oracle.
+
+Recipe (one numpy ``Generator(PCG64(seed))``, draws in this fixed order, all float32):
+
+1. x ~ N(0, 1), shape (B, L, Di)
+2. z ~ N(0, 1), shape (B, L, Di)
+3. dt ~ N(0, 0.5^2), shape (B, L, Di)   (the pre-bias step; the scan adds dt_bias)
+4. B_f, 5. C_f, 6. B_b, 7. C_b ~ N(0, 1), each shape (B, L, N)
+8. u_f, 9. u_b ~ U(ln 1e-3, ln 1e-1), each shape (Di,): dt0 = exp(u) is log-uniform in
+   [1e-3, 1e-1] and dt_bias = dt0 + log(-expm1(-dt0)), the value whose softplus is dt0.
+
+A_f = A_b = -(n+1) for n = 0..N-1, the same for every channel; D_f = D_b = 1.
+For bf16 workloads, x, z, dt, B_*, C_* are rounded float32 -> bf16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import Workload
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); return the uint16 bits.
+    NaN stays NaN (quiet)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+    nan = np.isnan(a)
+    if nan.any():
+        rounded = np.where(nan, ((u >> 16) | 0x40).astype(np.uint32), rounded)
+    return (rounded & 0xFFFF).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bits (uint16) to float32 exactly."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to_io(a: np.ndarray, io_dtype: str) -> np.ndarray:
+    """float32 values exactly representable in io_dtype (bf16 rounding is RNE)."""
+    if io_dtype == "f32":
+        return np.ascontiguousarray(a, dtype=np.float32)
+    if io_dtype == "bf16":
+        return bf16_bits_to_f32(f32_to_bf16_bits(a))
+    raise ValueError(f"unsupported io dtype {io_dtype!r}")
+
+
+TENSOR_NAMES = ("x", "z", "dt", "B_f", "C_f", "B_b", "C_b")
+PARAM_NAMES = ("A_f", "A_b", "D_f", "D_b", "dt_bias_f", "dt_bias_b")
+
+
+def make_inputs(batch: int, seqlen: int, d_inner: int, d_state: int = 16, io_dtype: str = "f32",
+                seed: int = 0) -> dict:
+    """Draw one seeded input set. Returns float32 numpy arrays; the I/O tensors already hold
+    values exactly representable in ``io_dtype``. Keys: TENSOR_NAMES + PARAM_NAMES."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, L, Di, N = batch, seqlen, d_inner, d_state
+    out = {}
+    out["x"] = rng.standard_normal((B, L, Di), dtype=np.float32)
+    out["z"] = rng.standard_normal((B, L, Di), dtype=np.float32)
+    out["dt"] = (np.float32(0.5) * rng.standard_normal((B, L, Di), dtype=np.float32)).astype(np.float32)
+    for name in ("B_f", "C_f", "B_b", "C_b"):
+        out[name] = rng.standard_normal((B, L, N), dtype=np.float32)
+    for name in ("dt_bias_f", "dt_bias_b"):
+        u = rng.uniform(np.log(1e-3), np.log(1e-1), size=Di)
+        dt0 = np.exp(u)
+        out[name] = (dt0 + np.log(-np.expm1(-dt0))).astype(np.float32)
+    a_row = -np.arange(1, N + 1, dtype=np.float32)
+    out["A_f"] = np.ascontiguousarray(np.broadcast_to(a_row, (Di, N)))
+    out["A_b"] = out["A_f"].copy()
+    out["D_f"] = np.ones(Di, dtype=np.float32)
+    out["D_b"] = np.ones(Di, dtype=np.float32)
+    for name in TENSOR_NAMES:
+        out[name] = round_to_io(out[name], io_dtype)
+    return out
+
+
+def make_workload_inputs(w: Workload) -> dict:
+    return make_inputs(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, w.seed)
+
+
+def random_params(d_inner: int, d_state: int, seed: int) -> dict:
+    """Per-direction parameters that differ between directions and across channels and states
+    (A in [-4, -0.05), D in [0.5, 1.5), dt_bias in [-5, 0.5)). Used by tests that must tell the
+    forward parameters from the backward ones, which the default recipe (A_f = A_b, D_f = D_b)
+    cannot."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for sfx in ("f", "b"):
+        out["A_" + sfx] = (-rng.uniform(0.05, 4.0, size=(d_inner, d_state))).astype(np.float32)
+        out["D_" + sfx] = rng.uniform(0.5, 1.5, size=d_inner).astype(np.float32)
+        out["dt_bias_" + sfx] = rng.uniform(-5.0, 0.5, size=d_inner).astype(np.float32)
+    return out

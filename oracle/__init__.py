@@ -1,0 +1,150 @@
+"""Float64 CPU oracle for the bidirectional selective scan.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-baseline leg are
+the only code that may import, build or call this package. The product path
+(``bidirectional_selective_scan_amd``) never imports it, and this package imports nothing from
+the product path: the two share no code. Inputs reach both from the seeded generator module.
+
+The arithmetic lives in ``vimscan_oracle.c`` (plain C, double precision, OpenMP over
+(batch, channel) pairs, a sequential loop over tokens inside each pair); its header states the
+definition it follows and the passages of the source pages each step comes from. This module
+builds it with gcc and calls it through ctypes.
+
+Every part of the oracle is pinned by the ``not gpu`` tests against results fixed outside it:
+the SSD quadratic (matrix) form by brute force, the convolution form and the geometric-series
+closed form for a time-invariant system, the B = 0 skip path, the reversed-scan symmetry, the
+bidirectional-sum identity at A = 0, folding with a periodic reset, the worked one-step and
+decay examples, and a first-order IIR filter from scipy. No function here is parity unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vimscan_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_BUILD_DIR, "libvimscan_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc -O2 -fopenmp into oracle/_build/. Returns the .so path."""
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _declare(lib):
+    lib.vimscan_oracle_bidir_f64.restype = ctypes.c_int
+    lib.vimscan_oracle_bidir_f64.argtypes = [_D] * 13 + [ctypes.c_int64] * 5 + [_D] * 3 + [ctypes.c_int]
+    lib.vimscan_oracle_softplus.restype = ctypes.c_double
+    lib.vimscan_oracle_softplus.argtypes = [ctypes.c_double]
+    lib.vimscan_oracle_silu.restype = ctypes.c_double
+    lib.vimscan_oracle_silu.argtypes = [ctypes.c_double]
+    lib.vimscan_oracle_max_threads.restype = ctypes.c_int
+    lib.vimscan_oracle_max_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=False)
+            _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def load_variant(so_path: str):
+    """Open another build of the oracle's C source (the tests compile deliberately broken
+    copies to show that the pins catch each mistake)."""
+    return _declare(ctypes.CDLL(so_path))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_D)
+
+
+ARG_ORDER = ("x", "dt", "z", "B_f", "C_f", "B_b", "C_b", "A_f", "A_b", "D_f", "D_b",
+             "dt_bias_f", "dt_bias_b")
+
+
+def bidir_fwd(inputs: dict, seg_len: int = 0, return_parts: bool = False, nthreads: int = 0,
+              lib=None):
+    """y = silu(z) * (y_fwd + y_bwd) in float64 for the arrays in ``inputs`` (keys as
+    ``ARG_ORDER``; any float dtype, widened exactly to float64).
+
+    Shapes: x, dt, z (B, L, Di); B_*, C_* (B, L, N); A_* (Di, N); D_*, dt_bias_* (Di,).
+    Returns y, or (y, y_fwd, y_bwd) with ``return_parts``. ``lib`` selects another build
+    (see ``load_variant``)."""
+    lib = lib if lib is not None else _load()
+    arrs = [_f64(inputs[k]) for k in ARG_ORDER]
+    x = arrs[0]
+    if x.ndim != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner)")
+    Bsz, L, Di = x.shape
+    N = arrs[3].shape[-1]
+    expect = {"x": (Bsz, L, Di), "dt": (Bsz, L, Di), "z": (Bsz, L, Di), "B_f": (Bsz, L, N),
+              "C_f": (Bsz, L, N), "B_b": (Bsz, L, N), "C_b": (Bsz, L, N), "A_f": (Di, N),
+              "A_b": (Di, N), "D_f": (Di,), "D_b": (Di,), "dt_bias_f": (Di,), "dt_bias_b": (Di,)}
+    for k, a in zip(ARG_ORDER, arrs):
+        if a.shape != expect[k]:
+            raise ValueError(f"{k}: shape {a.shape}, expected {expect[k]}")
+    y = np.empty((Bsz, L, Di), dtype=np.float64)
+    yf = np.empty_like(y) if return_parts else None
+    yb = np.empty_like(y) if return_parts else None
+    null = ctypes.cast(None, _D)
+    rc = lib.vimscan_oracle_bidir_f64(*[_ptr(a) for a in arrs], Bsz, L, Di, N, int(seg_len),
+                                      _ptr(y), _ptr(yf) if yf is not None else null,
+                                      _ptr(yb) if yb is not None else null, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return (y, yf, yb) if return_parts else y
+
+
+def softplus(v: float) -> float:
+    return _load().vimscan_oracle_softplus(float(v))
+
+
+def silu(v: float) -> float:
+    return _load().vimscan_oracle_silu(float(v))
+
+
+def max_threads() -> int:
+    return _load().vimscan_oracle_max_threads()
+
+
+def sample_channels(inputs: dict, seg_len: int, b_idx, d_idx, nthreads: int = 0):
+    """Oracle outputs for selected (b, d) channels only, every token: returns y[len(b_idx),
+    L, len(d_idx)]. Channels are independent, so this slices the inputs to the chosen batch
+    rows and channels and runs the full definition on that slice."""
+    b_idx = np.asarray(b_idx)
+    d_idx = np.asarray(d_idx)
+    sub = {}
+    for k in ("x", "dt", "z"):
+        sub[k] = np.asarray(inputs[k])[b_idx][:, :, d_idx]
+    for k in ("B_f", "C_f", "B_b", "C_b"):
+        sub[k] = np.asarray(inputs[k])[b_idx]
+    for k in ("A_f", "A_b"):
+        sub[k] = np.asarray(inputs[k])[d_idx]
+    for k in ("D_f", "D_b", "dt_bias_f", "dt_bias_b"):
+        sub[k] = np.asarray(inputs[k])[d_idx]
+    return bidir_fwd(sub, seg_len=seg_len, nthreads=nthreads)

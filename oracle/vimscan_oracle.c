@@ -1,0 +1,151 @@
+/*
+ * Float64 CPU oracle for the bidirectional selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, plain definition that the HIP path is
+ * checked against. Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * build, load or call it. It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes, for every batch row b and channel d (all in double precision):
+ *
+ *   Discretisation (VSSD page, section 4.1.2): the discrete transition is exp(delta * A) and
+ *   the discrete input matrix is taken as delta * B (the page's first-order form, not the exact
+ *   zero-order-hold one). delta = softplus(dt + dt_bias) is the selective step size: delta, B
+ *   and C depend on the token (VSSD page, section 4.1.4).
+ *
+ *   Recurrence (VSSD page, section 4.2.1.3, the linear form of SSD; A is diagonal per
+ *   (channel, state) as in S6):
+ *       h_t[n] = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B_t[n] * x_t,   h before t=0 is 0
+ *   Readout with the skip term (Mamba2D page, "standard Mamba 1D formula": y = C h + D x):
+ *       y_t = sum_n C_t[n] * h_t[n] + D[d] * x_t
+ *
+ *   Directions (Vim page, section 2.2): the forward path walks the tokens in raster order
+ *   t = 0..L-1 with (A_f, B_f, C_f, D_f, dt_bias_f); the backward path walks them in reverse,
+ *   t = L-1..0, with (A_b, B_b, C_b, D_b, dt_bias_b):
+ *       g_t[n] = exp(delta^b_t * A_b[d,n]) * g_{t+1}[n] + delta^b_t * B_b_t[n] * x_t,  g after L-1 is 0
+ *       yb_t   = sum_n C_b_t[n] * g_t[n] + D_b[d] * x_t
+ *   Every tensor is indexed by the natural token index t in both directions, and yb lands at t.
+ *
+ *   Output: y_t = silu(z_t) * (yf_t + yb_t), silu(v) = v / (1 + exp(-v)).
+ *
+ *   Periodic reset (SF-Mamba page, "Batch folding and periodic state reset"): with
+ *   seg_len > 0 the discrete transition is forced to 0 at the first token of every segment the
+ *   scan enters, i.e. the state is set to 0 before the update: forward at t % seg_len == 0,
+ *   backward at (t + 1) % seg_len == 0. seg_len == 0 means no reset.
+ *
+ * Layouts (row-major, last index fastest):
+ *   x, dt, z, y, yf, yb : [batch][seqlen][d_inner]
+ *   B_f, C_f, B_b, C_b  : [batch][seqlen][d_state]
+ *   A_f, A_b            : [d_inner][d_state]
+ *   D_f, D_b, dt_bias_* : [d_inner]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(v) = log(1 + exp(v)), evaluated without overflow and without a threshold. */
+double vimscan_oracle_softplus(double v) {
+    if (v > 0.0) return v + log1p(exp(-v));
+    return log1p(exp(v));
+}
+
+/* silu(v) = v * sigmoid(v) = v / (1 + exp(-v)). */
+double vimscan_oracle_silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* One direction over one (b, d) channel. step = +1 (forward) or -1 (backward).
+ * out[t] receives that direction's readout at the natural index t. */
+static void scan_one_direction(const double* x, const double* dt, const double* Bm, const double* Cm,
+                               const double* A, double Dd, double dt_bias, int64_t b, int64_t d,
+                               int64_t L, int64_t Di, int64_t N, int64_t seg_len, int step,
+                               double* h, double* out) {
+    for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+    for (int64_t k = 0; k < L; ++k) {
+        const int64_t t = (step > 0) ? k : (L - 1 - k);
+        if (seg_len > 0) {
+            const int64_t entry = (step > 0) ? t : (t + 1);
+            if (entry % seg_len == 0) {
+                for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+            }
+        }
+        const double xt = x[(b * L + t) * Di + d];
+        const double delta = vimscan_oracle_softplus(dt[(b * L + t) * Di + d] + dt_bias);
+        const double* Bt = Bm + (b * L + t) * N;
+        const double* Ct = Cm + (b * L + t) * N;
+        double y = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            const double abar = exp(delta * A[d * N + n]);
+            h[n] = abar * h[n] + delta * Bt[n] * xt;
+            y += Ct[n] * h[n];
+        }
+        out[t] = y + Dd * xt;
+    }
+}
+
+/* Returns 0 on success, -1 on a bad argument, -2 on allocation failure.
+ * yf and yb may be NULL; when given they receive the two branch outputs. nthreads <= 0 uses
+ * the OpenMP default. */
+int vimscan_oracle_bidir_f64(const double* x, const double* dt, const double* z,
+                             const double* B_f, const double* C_f, const double* B_b,
+                             const double* C_b, const double* A_f, const double* A_b,
+                             const double* D_f, const double* D_b, const double* dt_bias_f,
+                             const double* dt_bias_b, int64_t batch, int64_t seqlen,
+                             int64_t d_inner, int64_t d_state, int64_t seg_len, double* y,
+                             double* yf, double* yb, int nthreads) {
+    if (!x || !dt || !z || !B_f || !C_f || !B_b || !C_b || !A_f || !A_b || !D_f || !D_b ||
+        !dt_bias_f || !dt_bias_b || !y)
+        return -1;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || seg_len < 0) return -1;
+    if (seg_len > 0 && seqlen % seg_len != 0) return -1;
+    const int64_t B = batch, L = seqlen, Di = d_inner, N = d_state;
+    if (B == 0 || L == 0 || Di == 0) return 0;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * (size_t)N);
+        double* of = (double*)malloc(sizeof(double) * (size_t)L);
+        double* ob = (double*)malloc(sizeof(double) * (size_t)L);
+        const int ok = (h && of && ob);
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+        /* every thread reaches the worksharing loop; one without buffers skips its share */
+#pragma omp for collapse(2) schedule(static)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t d = 0; d < Di; ++d) {
+                if (!ok) continue;
+                scan_one_direction(x, dt, B_f, C_f, A_f, D_f[d], dt_bias_f[d], b, d, L, Di, N,
+                                   seg_len, +1, h, of);
+                scan_one_direction(x, dt, B_b, C_b, A_b, D_b[d], dt_bias_b[d], b, d, L, Di, N,
+                                   seg_len, -1, h, ob);
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t i = (b * L + t) * Di + d;
+                    y[i] = vimscan_oracle_silu(z[i]) * (of[t] + ob[t]);
+                    if (yf) yf[i] = of[t];
+                    if (yb) yb[i] = ob[t];
+                }
+            }
+        }
+        free(h);
+        free(of);
+        free(ob);
+    }
+    return err;
+}
+
+/* Number of threads an OpenMP parallel region would use right now (for reporting). */
+int vimscan_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

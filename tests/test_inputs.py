@@ -1,0 +1,58 @@
+"""The seeded input generator: determinism, the stated distributions, bf16 rounding."""
+import numpy as np
+import pytest
+import torch
+
+from bidirectional_selective_scan_amd.configs import WORKLOADS
+from bidirectional_selective_scan_amd.inputs import (bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
+                                                     round_to_io)
+
+
+def test_deterministic_and_seed_dependent():
+    a = make_inputs(2, 65, 32, 16, "f32", 0)
+    b = make_inputs(2, 65, 32, 16, "f32", 0)
+    c = make_inputs(2, 65, 32, 16, "f32", 1)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+    assert not np.array_equal(a["x"], c["x"])
+
+
+def test_distributions():
+    inp = make_inputs(4, 197, 384, 16, "f32", 0)
+    assert abs(inp["x"].std() - 1) < 0.01 and abs(inp["x"].mean()) < 0.01
+    assert abs(inp["dt"].std() - 0.5) < 0.005
+    assert abs(inp["B_b"].std() - 1) < 0.02
+    dt0 = np.log1p(np.exp(inp["dt_bias_f"].astype(np.float64)))   # softplus recovers dt0
+    assert dt0.min() >= 1e-3 * (1 - 1e-5) and dt0.max() <= 1e-1 * (1 + 1e-5)
+    np.testing.assert_array_equal(inp["A_f"][5], -np.arange(1, 17, dtype=np.float32))
+    np.testing.assert_array_equal(inp["D_b"], np.ones(384, np.float32))
+    assert not np.array_equal(inp["dt_bias_f"], inp["dt_bias_b"])
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.4e38, -1e-40, np.inf, -np.inf],
+                                 np.float32)])
+    ours = bf16_bits_to_f32(f32_to_bf16_bits(v))
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    nan = bf16_bits_to_f32(f32_to_bf16_bits(np.array([np.nan], np.float32)))
+    assert np.isnan(nan).all()
+
+
+@pytest.mark.parametrize("w", WORKLOADS[:3], ids=lambda w: w.name)
+def test_io_values_representable(w):
+    inp = make_inputs(2, 9, w.d_inner, 16, w.io_dtype, 0)
+    for k in ("x", "z", "dt", "B_f", "C_b"):
+        np.testing.assert_array_equal(round_to_io(inp[k], w.io_dtype), inp[k])
+
+
+def test_workload_table():
+    names = [w.name for w in WORKLOADS]
+    assert len(set(names)) == 5
+    vim_s = WORKLOADS[2]
+    assert (vim_s.batch, vim_s.seqlen, vim_s.d_inner, vim_s.io_dtype) == (128, 197, 768, "bf16")
+    assert vim_s.algorithmic_bytes() == 158_265_344
+    folded = WORKLOADS[4]
+    assert folded.seqlen == 256 * 51 and folded.seg_len == 51
