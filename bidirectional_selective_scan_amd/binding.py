@@ -1,0 +1,178 @@
+"""Thin ctypes binding of ``libvimscan.so`` (C ABI in include/vimscan.h).
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are checked, torch supplies the
+device memory (output and workspace) and the current stream, and every step of the scan runs in
+the library's HIP kernels. If the library is not built, calls raise; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libvimscan.so"
+_lock = threading.Lock()
+_lib = None
+
+VIMSCAN_F32 = 0
+VIMSCAN_BF16 = 1
+VIMSCAN_FLAG_GENERAL_DECAY = 1
+
+class VimscanError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"vimscan status {status}: {text}")
+        self.status = status
+
+
+class _Launch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
+                ("d_state", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int64), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("sequences", ctypes.c_int64), ("seq_tokens", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
+                ("chunks", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("kernels", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+
+EXPORTED = ("vimscan_bidir_fwd", "vimscan_plan_launch", "vimscan_workspace_bytes", "vimscan_status_string",
+            "vimscan_version")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load_library():
+    """Open libvimscan.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = lib_path()
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+            lib = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            lib.vimscan_bidir_fwd.restype = ctypes.c_int
+            lib.vimscan_bidir_fwd.argtypes = [vp] * 13 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
+            lib.vimscan_plan_launch.restype = ctypes.c_int
+            lib.vimscan_plan_launch.argtypes = [ctypes.POINTER(_Launch), ctypes.c_int64, ctypes.POINTER(_Plan)]
+            lib.vimscan_workspace_bytes.restype = ctypes.c_int
+            lib.vimscan_workspace_bytes.argtypes = [ctypes.POINTER(_Launch), ctypes.c_int64,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+            lib.vimscan_status_string.restype = ctypes.c_char_p
+            lib.vimscan_status_string.argtypes = [ctypes.c_int]
+            lib.vimscan_version.restype = ctypes.c_char_p
+            lib.vimscan_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().vimscan_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise VimscanError(status, status_string(status))
+
+
+def _io_code(dtype) -> int:
+    if dtype == torch.float32:
+        return VIMSCAN_F32
+    if dtype == torch.bfloat16:
+        return VIMSCAN_BF16
+    raise TypeError(f"io dtype must be float32 or bfloat16, got {dtype}")
+
+
+def make_launch(batch, seqlen, d_inner, d_state=16, io_dtype=VIMSCAN_BF16, chunk_len=0, general_decay=False,
+                workspace=0, workspace_bytes=0, stream=0) -> _Launch:
+    return _Launch(int(batch), int(seqlen), int(d_inner), int(d_state), int(io_dtype),
+                   VIMSCAN_FLAG_GENERAL_DECAY if general_decay else 0, int(chunk_len), workspace or None,
+                   int(workspace_bytes), stream or None)
+
+
+def launch_info(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0) -> dict:
+    """The library's execution plan for a call with this shape (host only)."""
+    code = VIMSCAN_BF16 if io_dtype == "bf16" else VIMSCAN_F32
+    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len)
+    plan = _Plan()
+    _check(load_library().vimscan_plan_launch(ctypes.byref(launch), int(seg_len), ctypes.byref(plan)))
+    return {f: getattr(plan, f) for f, _ in _Plan._fields_ if f != "reserved"}
+
+
+def workspace_bytes(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0) -> int:
+    code = VIMSCAN_BF16 if io_dtype == "bf16" else VIMSCAN_F32
+    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len)
+    n = ctypes.c_size_t(0)
+    _check(load_library().vimscan_workspace_bytes(ctypes.byref(launch), int(seg_len), ctypes.byref(n)))
+    return n.value
+
+
+class PreparedCall:
+    """A validated call of the scan on fixed tensors: ``__call__`` only queues the kernels (one
+    ctypes call), for loops that re-run the same shapes. Arguments as ``bidir_fwd``; the stream is
+    torch's current stream for x's device at preparation time unless ``stream`` is given."""
+
+    def __init__(self, x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
+                 out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, stream=None):
+        lib = load_library()
+        ios = (x, dt, z, B_f, C_f, B_b, C_b)
+        params = (A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b)
+        if x.dim() != 3:
+            raise ValueError("x must be (batch, seqlen, d_inner)")
+        Bsz, L, Di = x.shape
+        N = B_f.shape[-1] if B_f.dim() == 3 else -1
+        dev = x.device
+        if dev.type != "cuda":
+            raise ValueError("inputs must be on a GPU device")
+        io = _io_code(x.dtype)
+        shapes = [(Bsz, L, Di)] * 3 + [(Bsz, L, N)] * 4
+        for t, shp in zip(ios, shapes):
+            if t.device != dev or t.dtype != x.dtype or tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError("x, dt, z (B,L,Di) and B_*, C_* (B,L,N) must share device and dtype and be "
+                                 "contiguous")
+        pshapes = [(Di, N), (Di, N), (Di,), (Di,), (Di,), (Di,)]
+        for t, shp in zip(params, pshapes):
+            if t.device != dev or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError("A_* (Di,N) and D_*, dt_bias_* (Di,) must be contiguous float32 on x's device")
+        if out is None:
+            out = torch.empty_like(x)
+        elif out.device != dev or out.dtype != x.dtype or out.shape != x.shape or not out.is_contiguous():
+            raise ValueError("out must match x")
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        launch = make_launch(Bsz, L, Di, N, io, chunk_len, general_decay, 0, 0, stream)
+        need = ctypes.c_size_t(0)
+        _check(lib.vimscan_workspace_bytes(ctypes.byref(launch), int(seg_len), ctypes.byref(need)))
+        if need.value > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+            launch.workspace = workspace.data_ptr()
+            launch.workspace_bytes = workspace.numel() * workspace.element_size()
+        self.out = out
+        self._keep = (ios, params, out, workspace)   # keep every buffer alive while prepared
+        self._launch = launch
+        self._fn = lib.vimscan_bidir_fwd
+        self._args = tuple(t.data_ptr() for t in ios + params) + (int(seg_len), out.data_ptr(), ctypes.byref(launch))
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
+def bidir_fwd(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
+              out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None):
+    """y = silu(z) * (forward selective scan + backward selective scan), on the GPU.
+
+    x, dt, z: (B, L, Di); B_*, C_*: (B, L, 16), all float32 or all bfloat16, contiguous, on one
+    CUDA(HIP) device. A_*: (Di, 16); D_*, dt_bias_*: (Di,), float32. seg_len: 0, or the period of
+    the state reset (must divide L). Returns y (B, L, Di) in x's dtype (``out`` if given).
+    Queued on torch's current stream for x's device; does not synchronise."""
+    return PreparedCall(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len, out,
+                        chunk_len, general_decay, workspace)()

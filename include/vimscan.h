@@ -1,0 +1,136 @@
+/*
+ * vimscan.h -- C ABI of the bidirectional selective scan on AMD MI355X (gfx950).
+ *
+ * The operation (Vision Mamba page, section 2.2 "bidirectional state-space modelling": a
+ * forward path over the tokens in raster order and a backward path over them in reverse, the
+ * two fused; the fusion here is the sum gated by SiLU(z)). For every batch row b, channel d:
+ *
+ *   delta_t   = softplus(dt[b,t,d] + dt_bias[d])                       (selective step size)
+ *   Abar_t[n] = exp(delta_t * A[d,n]),  Bbar_t[n] = delta_t * B[b,t,n]
+ *                 (discretisation: VSSD notes page, section 4.1.2, first-order form for B)
+ *   forward:  h_t = Abar_t * h_{t-1} + Bbar_t * x[b,t,d],  t = 0..L-1,  h_{-1} = 0
+ *   backward: g_t = Abar'_t * g_{t+1} + Bbar'_t * x[b,t,d], t = L-1..0,  g_L = 0
+ *                 (linear SSD form: VSSD notes page, section 4.2.1.3)
+ *   yf_t = C_f[b,t,:] . h_t + D_f[d] x[b,t,d];   yb_t = C_b[b,t,:] . g_t + D_b[d] x[b,t,d]
+ *                 (readout with skip term: Mamba2D page, "standard Mamba 1D formula")
+ *   y[b,t,d]  = silu(z[b,t,d]) * (yf_t + yb_t),   silu(v) = v / (1 + exp(-v))
+ *
+ * with the forward quantities taken from (A_f, B_f, C_f, D_f, dt_bias_f) and the backward ones
+ * from (A_b, B_b, C_b, D_b, dt_bias_b). The backward path reads the same buffers at descending
+ * t; nothing is flipped or copied. State (N = 16 floats per channel and direction) is fp32 and
+ * never leaves the chip except as chunk carries in the workspace.
+ *
+ * Periodic reset (SF-Mamba page, "Batch folding and periodic state reset"): with seg_len > 0
+ * the state is cleared before the update at the first token of every segment the scan enters
+ * (forward: t % seg_len == 0; backward: (t + 1) % seg_len == 0), so B short sequences of
+ * length T folded into one stream of length B*T give the same outputs as the unfolded batch.
+ *
+ * Layouts (row-major, last index fastest, all dense):
+ *   x, dt, z, y           [batch][seqlen][d_inner]   io dtype (fp32 or bf16)
+ *   B_f, C_f, B_b, C_b    [batch][seqlen][d_state]   io dtype
+ *   A_f, A_b              [d_inner][d_state]         fp32
+ *   D_f, D_b, dt_bias_*   [d_inner]                  fp32
+ * dt is the step before the bias is added. bf16 outputs are rounded to nearest even.
+ *
+ * Ownership and execution: every pointer is device memory owned by the caller; the library
+ * allocates and frees nothing and keeps no state between calls. Work is queued on the given
+ * stream and the call returns without synchronising. Inputs are read only; y must not overlap
+ * any input. All argument checks run on the host before any HIP call, so every error other
+ * than VIMSCAN_ERR_HIP leaves the device untouched.
+ */
+#ifndef VIMSCAN_H
+#define VIMSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum vimscan_status {
+    VIMSCAN_OK = 0,
+    VIMSCAN_ERR_NULL = -1,      /* a required pointer is NULL (launch, an input, or y) */
+    VIMSCAN_ERR_SHAPE = -2,     /* batch, seqlen or d_inner < 0; d_state != 16;
+                                   d_inner >= 2^22; or batch*seqlen*d_inner >= 2^31 */
+    VIMSCAN_ERR_SEGLEN = -3,    /* seg_len < 0, or seg_len > 0 and seqlen % seg_len != 0 */
+    VIMSCAN_ERR_DTYPE = -4,     /* io_dtype is not VIMSCAN_F32 or VIMSCAN_BF16 */
+    VIMSCAN_ERR_ALIGN = -5,     /* a pointer is not aligned: x, dt, z, y to the io element
+                                   size; B_*, C_* and the fp32 parameters to 4 bytes */
+    VIMSCAN_ERR_ALIAS = -6,     /* y overlaps an input */
+    VIMSCAN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than vimscan_workspace_bytes */
+    VIMSCAN_ERR_HIP = -8,       /* a kernel launch failed (hipGetLastError after launching) */
+    VIMSCAN_ERR_CHUNK = -9,     /* chunk_len < 0 */
+    VIMSCAN_ERR_FLAGS = -10     /* unknown bits in flags */
+};
+
+/* dtype of x, dt, z, B_*, C_* and y. */
+enum vimscan_io_dtype { VIMSCAN_F32 = 0, VIMSCAN_BF16 = 1 };
+
+/* flags */
+/* Evaluate exp(delta*A[d,n]) once per (token, channel, state) even when a channel's A row is
+   an arithmetic progression in n, for which the library otherwise forms the transitions as
+   exp(delta*A[d,0]) * exp(delta*(A[d,1]-A[d,0]))^n. Both give the defined result. */
+#define VIMSCAN_FLAG_GENERAL_DECAY 1
+
+/* Shape and launch description, passed by pointer to every entry point. */
+typedef struct vimscan_launch {
+    int64_t batch;          /* B >= 0 */
+    int64_t seqlen;         /* L >= 0 (the folded stream length when seg_len > 0) */
+    int64_t d_inner;        /* Di >= 0 */
+    int64_t d_state;        /* N; must be 16 */
+    int32_t io_dtype;       /* enum vimscan_io_dtype */
+    int32_t flags;          /* VIMSCAN_FLAG_* bits */
+    int64_t chunk_len;      /* 0: the library picks; > 0: tokens per chunk of the chunked scan
+                               (values >= the sequence length give a single pass) */
+    void* workspace;        /* device scratch of at least vimscan_workspace_bytes() bytes;
+                               may be NULL when that size is 0 */
+    size_t workspace_bytes; /* size of workspace */
+    void* stream;           /* hipStream_t to queue the work on; NULL = the null stream */
+} vimscan_launch;
+
+/* How a call with this launch is executed (for reporting and tests). */
+typedef struct vimscan_plan {
+    int64_t sequences;      /* independent sequences: batch, or batch*seqlen/seg_len */
+    int64_t seq_tokens;     /* tokens per independent sequence */
+    int64_t chunk_len;      /* tokens per chunk */
+    int64_t chunks;         /* chunks per sequence; 1 = single pass, no workspace */
+    int64_t workgroups;     /* workgroups of the main scan kernel */
+    int32_t kernels;        /* kernels launched per call: 1 (single pass) or 3 (chunked) */
+    int32_t reserved;
+    size_t workspace_bytes; /* scratch this call needs */
+} vimscan_plan;
+
+/*
+ * y = silu(z) * (forward scan + backward scan), as defined above, queued on launch->stream.
+ * x, dt, z, B_f, C_f, B_b, C_b and y are io-dtype device arrays; A_*, D_*, dt_bias_* are fp32
+ * device arrays. seg_len: 0 for no reset, else the reset period (must divide seqlen).
+ * Returns VIMSCAN_OK or a negative vimscan_status. Empty shapes (batch, seqlen or d_inner 0)
+ * are checked for shape, dtype, seg_len and flags and then return VIMSCAN_OK without launching;
+ * their pointers may be NULL.
+ */
+int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* B_f,
+                      const void* C_f, const void* B_b, const void* C_b, const float* A_f,
+                      const float* A_b, const float* D_f, const float* D_b,
+                      const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
+                      const vimscan_launch* launch);
+
+/* Fills *plan for a call with this launch and seg_len (workspace fields of launch are
+   ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */
+int vimscan_plan_launch(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan);
+
+/* Scratch bytes a call with this launch and seg_len needs (0 for a single pass). Host only. */
+int vimscan_workspace_bytes(const vimscan_launch* launch, int64_t seg_len, size_t* bytes);
+
+/* Static text for a status code; never NULL. */
+const char* vimscan_status_string(int status);
+
+/* Library version string, e.g. "vimscan 0.1.0 gfx950". */
+const char* vimscan_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VIMSCAN_H */

@@ -1,0 +1,160 @@
+"""The C ABI without a GPU: the library loads, exports every function include/vimscan.h declares,
+plans launches, and rejects bad arguments with the documented status before any HIP call.
+
+Every call here fails validation (or is host-only), so nothing reaches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bidirectional_selective_scan_amd import binding
+from bidirectional_selective_scan_amd.configs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vimscan.h")
+
+OK, NULL, SHAPE, SEGLEN, DTYPE, ALIGN, ALIAS, WORKSPACE, HIP, CHUNK, FLAGS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vimscan_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert "vimscan_bidir_fwd" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_status_strings(lib):
+    for code in range(0, -11, -1):
+        s = binding.status_string(code)
+        assert s and s != "unknown status"
+    assert binding.status_string(-99) == "unknown status"
+    assert binding.status_string(5) == "unknown status"
+    assert b"gfx950" in lib.vimscan_version()
+
+
+def test_plans_for_the_workloads(lib):
+    plans = {w.name: binding.launch_info(w.batch, w.seqlen, w.d_inner, 16, w.seg_len, w.io_dtype) for w in WORKLOADS}
+    vim_s = plans["vim_s_b128_l197_d768_bf16"]
+    assert (vim_s["chunks"], vim_s["kernels"], vim_s["workspace_bytes"]) == (1, 1, 0)
+    assert vim_s["workgroups"] == 128 * 12
+    folded = plans["folded_256x51_d1536_bf16"]
+    assert (folded["sequences"], folded["seq_tokens"], folded["chunks"]) == (256, 51, 1)
+    hi = plans["highres_b8_l1025_d768_bf16"]
+    assert hi["chunks"] > 1 and hi["kernels"] == 3 and hi["workspace_bytes"] > 0
+    assert hi["chunk_len"] * hi["chunks"] >= 1025 > hi["chunk_len"] * (hi["chunks"] - 1)
+    assert hi["workspace_bytes"] == 2 * 8 * hi["chunks"] * 17 * 768 * 4
+    # a forced chunk length is honoured and capped at 256 tokens
+    assert binding.launch_info(2, 197, 64, chunk_len=16)["chunks"] == 13
+    assert binding.launch_info(1, 1000, 64, chunk_len=5000)["chunk_len"] == 256
+
+
+def _launch(**kw):
+    base = dict(batch=2, seqlen=12, d_inner=64, d_state=16, io_dtype=binding.VIMSCAN_F32, chunk_len=0,
+                general_decay=False, workspace=0, workspace_bytes=0, stream=0)
+    base.update(kw)
+    return binding.make_launch(**base)
+
+
+def _call(lib, launch, ptrs=None, seg_len=0, y=None):
+    # distinct, far-apart fake device addresses: never dereferenced, every case fails validation
+    p = ptrs or [0x10000000 * (i + 1) for i in range(13)]
+    y = 0x7F0000000 if y is None else y
+    return lib.vimscan_bidir_fwd(*p, seg_len, y, ctypes.byref(launch) if launch is not None else None)
+
+
+def test_null_arguments(lib):
+    assert _call(lib, None) == NULL
+    ptrs = [0x10000000 * (i + 1) for i in range(13)]
+    for i in range(13):
+        p = list(ptrs)
+        p[i] = 0
+        assert _call(lib, _launch(d_state=7), p) == SHAPE   # shape is checked first
+        assert _call(lib, _launch(seqlen=12), p, seg_len=5) == SEGLEN
+    # empty shapes launch nothing and accept NULL pointers
+    assert _call(lib, _launch(batch=0), [0] * 13, y=0) == OK
+    assert _call(lib, _launch(d_inner=0), [0] * 13, y=0) == OK
+    assert _call(lib, _launch(batch=0, d_state=3), [0] * 13, y=0) == SHAPE
+    p = list(ptrs)
+    p[4] = 0
+    launch = _launch(batch=1, seqlen=1, d_inner=1)
+    assert _call(lib, launch, p) == NULL
+    assert _call(lib, launch, ptrs, y=0) == NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_state=8), SHAPE), (dict(batch=-1), SHAPE), (dict(seqlen=-3), SHAPE), (dict(d_inner=-1), SHAPE),
+    (dict(batch=1 << 20, seqlen=1 << 10, d_inner=1 << 2), SHAPE),
+    (dict(io_dtype=2), DTYPE), (dict(chunk_len=-1), CHUNK), (dict(flags_raw=4), FLAGS),
+])
+def test_bad_launch_fields(lib, kw, code):
+    flags = kw.pop("flags_raw", None)
+    launch = _launch(**kw)
+    if flags is not None:
+        launch.flags = flags
+    assert _call(lib, launch) == code
+
+
+def test_seg_len(lib):
+    assert _call(lib, _launch(seqlen=12), seg_len=-1) == SEGLEN
+    assert _call(lib, _launch(seqlen=12), seg_len=5) == SEGLEN
+    assert _call(lib, _launch(seqlen=12), seg_len=24) == SEGLEN
+
+
+def test_alignment(lib):
+    ptrs = [0x10000000 * (i + 1) for i in range(13)]
+    bad = list(ptrs)
+    bad[0] += 2                                   # fp32 x on a 2-byte boundary
+    assert _call(lib, _launch(), bad) == ALIGN
+    bad = list(ptrs)
+    bad[3] += 2                                   # B_f must be 4-byte aligned even for bf16
+    assert _call(lib, _launch(io_dtype=binding.VIMSCAN_BF16), bad) == ALIGN
+    bad = list(ptrs)
+    bad[7] += 1                                   # A_f
+    assert _call(lib, _launch(), bad) == ALIGN
+    assert _call(lib, _launch(), ptrs, y=0x7F0000001) == ALIGN
+
+
+def test_alias(lib):
+    ptrs = [0x10000000 * (i + 1) for i in range(13)]
+    # y starts inside x's range (x holds 2*12*64*4 bytes)
+    assert _call(lib, _launch(), ptrs, y=ptrs[0] + 256) == ALIAS
+    # y ends inside A_b
+    S = 2 * 12 * 64 * 4
+    assert _call(lib, _launch(), ptrs, y=ptrs[8] - S + 4) == ALIAS
+    # disjoint: touching but not overlapping is fine -> would launch, so only check the plan here
+
+
+def test_workspace_required_for_chunked_plans(lib):
+    launch = _launch(batch=1, seqlen=1025, d_inner=64)
+    need = ctypes.c_size_t(0)
+    assert lib.vimscan_workspace_bytes(ctypes.byref(launch), 0, ctypes.byref(need)) == OK and need.value > 0
+    assert _call(lib, launch) == WORKSPACE
+    launch.workspace = 0x50000000
+    launch.workspace_bytes = need.value - 4
+    assert _call(lib, launch) == WORKSPACE
+    launch.workspace_bytes = need.value
+    launch.workspace = 0x10000000 + 64       # overlaps x
+    assert _call(lib, launch) == ALIAS
+
+
+def test_workspace_bytes_rejects_bad_shapes(lib):
+    need = ctypes.c_size_t(0)
+    assert lib.vimscan_workspace_bytes(ctypes.byref(_launch(d_state=4)), 0, ctypes.byref(need)) == SHAPE
+    assert lib.vimscan_workspace_bytes(ctypes.byref(_launch()), 0, None) == NULL
+    assert lib.vimscan_workspace_bytes(None, 0, ctypes.byref(need)) == NULL

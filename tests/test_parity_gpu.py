@@ -1,0 +1,155 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, on the GPU.
+
+Tolerances (see gpu_helpers): fp32 io |e| <= 1e-4 (1 + |y|); bf16 io |e| <= 2e-2 (|y| + rms(y)).
+Every input is seeded and synthetic (bidirectional_selective_scan_amd.inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bidirectional_selective_scan_amd import binding
+from bidirectional_selective_scan_amd.configs import WORKLOADS
+from bidirectional_selective_scan_amd.inputs import make_inputs, make_workload_inputs, random_params
+from gpu_helpers import assert_close, run_gpu, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, L, Di, io, seed, random=False):
+    inp = make_inputs(B, L, Di, 16, io, seed)
+    if random:
+        inp.update(random_params(Di, 16, seed + 7))
+    return inp
+
+
+@pytest.mark.parametrize("general", [False, True], ids=["auto", "general_decay"])
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
+def test_workload_full_size(w, general):
+    """Every element of each workload at its full size, in the launch configuration the
+    benchmark times (the library's own plan)."""
+    inp = make_workload_inputs(w)
+    dev = to_device(inp, w.io_dtype)
+    y = to_f64(run_gpu(dev, seg_len=w.seg_len, general_decay=general))
+    ref = oracle.bidir_fwd(inp, seg_len=w.seg_len)
+    assert np.isfinite(y).all()
+    assert_close(y, ref, w.io_dtype, w.name)
+
+
+SHAPES = [
+    # B, L, Di, seg_len, chunk_len
+    (1, 1, 1, 0, 0),
+    (2, 2, 3, 0, 0),
+    (1, 3, 64, 0, 0),
+    (3, 63, 65, 0, 0),
+    (2, 64, 128, 0, 0),
+    (2, 65, 130, 0, 0),
+    (1, 200, 70, 0, 0),
+    (2, 257, 64, 0, 0),      # longer than one chunk: chunked path, ragged last chunk
+    (1, 300, 96, 0, 0),
+    (1, 1025, 64, 0, 0),
+    (2, 197, 64, 0, 16),     # forced chunking, ragged tail (197 = 12*16 + 5)
+    (2, 197, 64, 0, 1),      # one token per chunk
+    (2, 197, 100, 0, 64),
+    (1, 120, 64, 12, 0),     # folded: 10 segments of 12
+    (1, 120, 64, 12, 5),     # folded, chunks that do not divide the segment
+    (2, 102, 33, 51, 0),
+    (1, 60, 64, 1, 0),       # reset every token
+    (3, 256, 64, 0, 0),      # the longest single-pass sequence
+]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("random", [False, True], ids=["s4d_A", "random_A"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_L%d_D%d_seg%d_chunk%d" % s)
+def test_shapes(shape, random, io):
+    B, L, Di, seg, chunk = shape
+    inp = _case(B, L, Di, io, seed=L * 31 + Di, random=random)
+    dev = to_device(inp, io)
+    y = to_f64(run_gpu(dev, seg_len=seg, chunk_len=chunk))
+    ref = oracle.bidir_fwd(inp, seg_len=seg)
+    assert_close(y, ref, io, f"{shape} random={random}")
+
+
+def test_direction_parameters_are_routed():
+    """Forward and backward parameters differ (A, D, dt_bias, B, C): a swap on the GPU fails."""
+    inp = _case(2, 97, 128, "f32", seed=3, random=True)
+    dev = to_device(inp, "f32")
+    y = to_f64(run_gpu(dev))
+    assert_close(y, oracle.bidir_fwd(inp), "f32", "routed")
+    swapped = dict(inp)
+    for a, b in (("A_f", "A_b"), ("D_f", "D_b"), ("dt_bias_f", "dt_bias_b")):
+        swapped[a], swapped[b] = inp[b], inp[a]
+    assert np.abs(oracle.bidir_fwd(swapped) - y).max() > 1e-2
+
+
+def test_deterministic():
+    w = WORKLOADS[2]
+    inp = make_inputs(16, w.seqlen, w.d_inner, 16, w.io_dtype, 5)
+    dev = to_device(inp, w.io_dtype)
+    a = run_gpu(dev).clone()
+    b = run_gpu(dev).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("chunk", [0, 17])
+def test_folded_equals_unfolded_bitwise(chunk):
+    """Folding 40 sequences of 51 tokens into one stream with a reset every 51 tokens gives the
+    unfolded outputs bit for bit, at the same (sequence, token, channel) index."""
+    k, T, Di = 40, 51, 192
+    unf = make_inputs(k, T, Di, 16, "bf16", 11)
+    dev_u = to_device(unf, "bf16")
+    y_u = run_gpu(dev_u, chunk_len=chunk)
+    dev_f = {n: (t.reshape((1, k * T) + tuple(t.shape[2:])) if n in ("x", "dt", "z", "B_f", "C_f", "B_b", "C_b")
+                 else t) for n, t in dev_u.items()}
+    y_f = run_gpu(dev_f, seg_len=T, chunk_len=chunk)
+    assert torch.equal(y_f.reshape(k, T, Di).view(torch.int16), y_u.view(torch.int16))
+    ref = oracle.bidir_fwd(unf)
+    assert_close(to_f64(y_u), ref, "bf16", "unfolded")
+
+
+def test_reset_isolates_segments():
+    """NaN in one folded segment changes no bit of any other segment."""
+    T, nseg, Di = 51, 8, 128
+    inp = make_inputs(1, T * nseg, Di, 16, "bf16", 12)
+    dev = to_device(inp, "bf16")
+    y0 = run_gpu(dev, seg_len=T).clone()
+    dev["x"][0, 3 * T:4 * T] = float("nan")
+    dev["B_f"][0, 3 * T + 5] = float("inf")
+    y1 = run_gpu(dev, seg_len=T)
+    keep = torch.ones(T * nseg, dtype=torch.bool)
+    keep[3 * T:4 * T] = False
+    assert torch.equal(y1[0, keep].view(torch.int16), y0[0, keep].view(torch.int16))
+    assert torch.isnan(y1[0, 3 * T:4 * T].float()).any()
+
+
+@pytest.mark.parametrize("shape", [(0, 10, 8), (2, 0, 8), (2, 10, 0)])
+def test_empty_shapes(shape):
+    B, L, Di = shape
+    inp = make_inputs(B, L, Di, 16, "f32", 0)
+    dev = to_device(inp, "f32")
+    y = run_gpu(dev)
+    assert tuple(y.shape) == (B, L, Di)
+
+
+def test_runs_on_a_side_stream():
+    inp = _case(4, 197, 256, "bf16", seed=9)
+    dev = to_device(inp, "bf16")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = run_gpu(dev)
+    s.synchronize()
+    assert_close(to_f64(y), oracle.bidir_fwd(inp), "bf16", "side stream")
+
+
+def test_errors_are_reported():
+    inp = _case(1, 12, 64, "f32", seed=1)
+    dev = to_device(inp, "f32")
+    with pytest.raises(binding.VimscanError):
+        run_gpu(dev, seg_len=5)                      # 12 % 5 != 0
+    with pytest.raises(binding.VimscanError):
+        run_gpu(dev, out=dev["x"])                   # output aliases an input
+    with pytest.raises(ValueError):
+        bad = dict(dev)
+        bad["B_f"] = dev["B_f"][:, :, :8].contiguous()   # N = 8
+        run_gpu(bad)
