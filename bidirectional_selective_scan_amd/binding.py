@@ -37,7 +37,7 @@ class _Launch(ctypes.Structure):
 class _Plan(ctypes.Structure):
     _fields_ = [("sequences", ctypes.c_int64), ("seq_tokens", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
                 ("chunks", ctypes.c_int64), ("workgroups", ctypes.c_int64), ("kernels", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+                ("park_in_workspace", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
 
 EXPORTED = ("vimscan_bidir_fwd", "vimscan_plan_launch", "vimscan_workspace_bytes", "vimscan_status_string",
@@ -103,7 +103,7 @@ def launch_info(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", 
     launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len)
     plan = _Plan()
     _check(load_library().vimscan_plan_launch(ctypes.byref(launch), int(seg_len), ctypes.byref(plan)))
-    return {f: getattr(plan, f) for f, _ in _Plan._fields_ if f != "reserved"}
+    return {f: getattr(plan, f) for f, _ in _Plan._fields_}
 
 
 def workspace_bytes(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0) -> int:

@@ -98,8 +98,10 @@ typedef struct vimscan_plan {
     int64_t chunks;         /* chunks per sequence; 1 = single pass, no workspace */
     int64_t workgroups;     /* workgroups of the main scan kernel */
     int32_t kernels;        /* kernels launched per call: 1 (single pass) or 3 (chunked) */
-    int32_t reserved;
-    size_t workspace_bytes; /* scratch this call needs */
+    int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
+                               workspace (long chunks); 0: through LDS */
+    size_t workspace_bytes; /* scratch this call needs: chunk carries when chunks > 1, plus
+                               chunk_len*64*4 bytes per workgroup when park_in_workspace */
 } vimscan_plan;
 
 /*
@@ -120,7 +122,8 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
    ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */
 int vimscan_plan_launch(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan);
 
-/* Scratch bytes a call with this launch and seg_len needs (0 for a single pass). Host only. */
+/* Scratch bytes a call with this launch and seg_len needs (0 for a single pass over short
+   sequences). Host only. */
 int vimscan_workspace_bytes(const vimscan_launch* launch, int64_t seg_len, size_t* bytes);
 
 /* Static text for a status code; never NULL. */

@@ -50,6 +50,7 @@ SHAPES = [
     (2, 197, 64, 0, 16),     # forced chunking, ragged tail (197 = 12*16 + 5)
     (2, 197, 64, 0, 1),      # one token per chunk
     (2, 197, 100, 0, 64),
+    (2, 400, 64, 0, 150),    # chunked with chunks long enough to park in the workspace
     (1, 120, 64, 12, 0),     # folded: 10 segments of 12
     (1, 120, 64, 12, 5),     # folded, chunks that do not divide the segment
     (2, 102, 33, 51, 0),
