@@ -144,13 +144,15 @@ struct ScanArgs {
     int T;         // tokens per chunk
     int K;         // chunks per sequence
     int ncb;       // channel blocks of 64
+    int subs;      // channel blocks per workgroup (1 or 2): 2 * subs waves per workgroup
     int general;   // 1: never use the arithmetic-progression transitions
 };
 
 // The state-independent part of one token, computed a token ahead of its state update.
 struct Prelude {
-    float delta, u, dx;  // softplus(dt + bias), delta*x, D*x
+    float delta, dx;     // softplus(dt + bias), D*x
     float e[kN];         // transitions exp(delta * A[d, n])
+    float ub[kN];        // inputs delta * x * B[n]
 };
 
 // Per-lane recurrence state of one direction over one channel.
@@ -181,11 +183,13 @@ struct Lane {
     }
 
     template <bool kProgression>
-    __device__ __forceinline__ Prelude prelude(float xv, float dtv) const {
+    __device__ __forceinline__ Prelude prelude(float xv, float dtv, const float (&Bv)[kN]) const {
         Prelude p;
         p.delta = softplus(dtv + bias);
-        p.u = p.delta * xv;
+        const float u = p.delta * xv;
         p.dx = Dd * xv;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) p.ub[n] = u * Bv[n];
         if (kProgression) {
             // e[n] = e0 * q^n along four independent chains of stride q^4
             const float q = fast_exp2(p.delta * da);
@@ -204,13 +208,13 @@ struct Lane {
         return p;
     }
 
-    // State update h = e*h + u*B; returns the readout C.h + D x.
+    // State update h = e*h + delta*x*B; returns the readout C.h + D x.
     template <bool kReadout>
-    __device__ __forceinline__ float update(const Prelude& p, const float (&Bv)[kN], const float (&Cv)[kN]) {
+    __device__ __forceinline__ float update(const Prelude& p, const float (&Cv)[kN]) {
         float acc[4] = {p.dx, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
-            h[n] = fmaf(p.u, Bv[n], h[n] * p.e[n]);
+            h[n] = fmaf(h[n], p.e[n], p.ub[n]);
             if (kReadout) acc[n & 3] = fmaf(Cv[n], h[n], acc[n & 3]);
         }
         return (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -218,20 +222,25 @@ struct Lane {
 };
 
 struct WgCoords {
-    int lid, seq, chunk, cb, lane, dir, d, dc, t0, t1;
+    int lid, seq, chunk, cb, lane, dir, sub, slot, d, dc, t0, t1;
     bool valid;
 };
 
 __device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a) {
     WgCoords c;
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int ncbw = (a.ncb + a.subs - 1) / a.subs;  // channel-block groups per sequence
     c.lid = lid;
-    c.cb = lid % a.ncb;
-    const int rest = lid / a.ncb;
+    const int cbw = lid % ncbw;
+    const int rest = lid / ncbw;
     c.chunk = rest % a.K;
     c.seq = rest / a.K;
     c.lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-    c.dir = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    c.dir = wave & 1;
+    c.sub = wave >> 1;
+    c.slot = lid * a.subs + c.sub;  // this wave pair's park region
+    c.cb = cbw * a.subs + c.sub;    // may be past the last block when ncb is odd: no lane stores
     c.d = c.cb * kWave + c.lane;
     c.valid = c.d < a.Di;
     c.dc = c.valid ? c.d : a.Di - 1;
@@ -248,12 +257,13 @@ enum WalkMode {
 };
 
 // Walk this wave's tokens k = kbeg..kend-1 of the chunk (forward: local token k; backward:
-// local token len-1-k). Per step k: the prelude of token k+1 is formed from a ring of
-// prefetched x/dt values (refilled kPrefetch tokens ahead); z and the parked value of token k
-// come from their own ring; token k's state update and readout run on the prelude formed a step
-// earlier; then the B/C rows of token k+1 are requested through the scalar unit, to be used
-// after the next prelude. Every prefetch index is clamped into the walk, so every load stays
-// inside the chunk.
+// local token len-1-k). Per step k: the prelude of token k+1 (including delta*x*B) is formed
+// from a ring of prefetched x/dt values (refilled kPrefetch tokens ahead) and the B row of
+// token k+1, after which the B row of token k+2 is requested through the scalar unit; z and
+// the parked value of token k come from their own ring; token k's state update and readout
+// run on the prelude formed a step earlier; then the C row of token k+2 is requested into the
+// VGPR slot token k's row just left. Every prefetch index is clamped into the walk, so every
+// load stays inside the chunk.
 template <typename IO, bool kProg, int kMode, bool kGlobalPark>
 __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park, int kbeg,
                                      int kend, float& dsum) {
@@ -273,7 +283,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const __amdgpu_buffer_rsrc_t rz = chunk_rsrc(static_cast<const E*>(a.z) + eoff, span);
     const __amdgpu_buffer_rsrc_t ry = chunk_rsrc(static_cast<E*>(a.y) + eoff, span);
     const __amdgpu_buffer_rsrc_t rp =
-        chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.lid) * a.T * kWave : nullptr,
+        chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.slot) * a.T * kWave : nullptr,
                    static_cast<uint32_t>(a.T) * kWave * 4);
     const float* Bs = a.Brow[c.dir] + row0 * kN;
     const float* Cs = a.Crow[c.dir] + row0 * kN;
@@ -299,10 +309,27 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             pr[j] = kGlobalPark ? __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kbeg + j), 0) : 0u;
         }
     }
-    float Bc[kN], Cc[kN];
-    ld_row(Bs + lt(kbeg) * kN, Bc);
-    if (kReadout) ld_row(Cs + lt(kbeg) * kN, Cc);
-    Prelude cur = ln.template prelude<kProg>(widen(IO{}, xr[0]), widen(IO{}, dr[0]));
+    // B rows (SGPRs) run one token ahead: B(k+1) is consumed by the prelude of token k+1 during
+    // step k. C rows travel as wave-uniform vector loads into a two-slot VGPR ring: C(k) is read
+    // by the readout of step k, after which C(k+2) is requested into its slot.
+    const __amdgpu_buffer_rsrc_t rC = chunk_rsrc(Cs, static_cast<uint32_t>(len) * (kN * 4));
+    auto crow = [&](int k, float (&v)[kN]) {
+        const uint32_t so = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lt(min(k, last)))) * (kN * 4);
+#pragma unroll
+        for (int q = 0; q < kN / 4; ++q) {
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(rC, 0, so + 16 * q, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[4 * q + i] = __uint_as_float(w[i]);
+        }
+    };
+    float Bn[kN], Cr[2][kN];
+    ld_row(Bs + lt(kbeg) * kN, Bn);
+    if (kReadout) {
+        crow(kbeg, Cr[0]);
+        crow(kbeg + 1, Cr[1]);
+    }
+    Prelude cur = ln.template prelude<kProg>(widen(IO{}, xr[0]), widen(IO{}, dr[0]), Bn);
+    ld_row(Bs + lt(min(kbeg + 1, last)) * kN, Bn);
     {
         const uint32_t so = toff(kbeg + P);
         xr[0] = ld_raw(IO{}, rx, vo, so);
@@ -312,25 +339,31 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     auto body = [&](int kk, int j) {
         const int jn = (j + 1) % P;
         const int tl = lt(kk);
-        // next token's prelude, then refill its x/dt slot kPrefetch tokens further on
-        const Prelude nxt = ln.template prelude<kProg>(widen(IO{}, xr[jn]), widen(IO{}, dr[jn]));
+        // Consume the ring slots before refilling them: the empty asm takes the widened values
+        // and orders every load after it, so a refill can reuse its slot's register and the loop
+        // needs no register copies (a copy would wait for the load just issued).
+        const float xn = widen(IO{}, xr[jn]), dn = widen(IO{}, dr[jn]);
+        float zv = 0.0f, pv = 0.0f;
+        if (kMode == kFinish) {
+            zv = widen(IO{}, zr[j]);
+            pv = __uint_as_float(pr[j]);
+        }
+        asm volatile("" ::"v"(xn), "v"(dn), "v"(zv), "v"(pv) : "memory");
         {
             const uint32_t so = toff(kk + 1 + P);
             xr[jn] = ld_raw(IO{}, rx, vo, so);
             dr[jn] = ld_raw(IO{}, rd, vo, so);
         }
-        // this token's z and parked value
-        float zv = 0.0f, pv = 0.0f;
         if (kMode == kFinish) {
-            zv = widen(IO{}, zr[j]);
-            pv = __uint_as_float(pr[j]);
             const uint32_t so = toff(kk + P);
             zr[j] = ld_raw(IO{}, rz, vo, so);
             if (kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
-        asm volatile("" ::: "memory");  // the loads above are issued before this token's stores
+        // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
+        const Prelude nxt = ln.template prelude<kProg>(xn, dn, Bn);
+        ld_row(Bs + lt(min(kk + 2, last)) * kN, Bn);
         if (kMode == kAggregate) dsum += cur.delta;
-        const float yv = ln.template update<kReadout>(cur, Bc, Cc);
+        const float yv = ln.template update<kReadout>(cur, Cr[j & 1]);
         if (kMode == kPark) {
             if (kGlobalPark)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), rp, vp,
@@ -342,11 +375,16 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             const float other = kGlobalPark ? pv : lds_park[tl * kWave + c.lane];
             if (c.valid) st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (yv + other));
         }
-        // the next token's B/C rows reuse this token's SGPRs; the next prelude covers their latency
-        const int rn = lt(min(kk + 1, last));
-        ld_row(Bs + rn * kN, Bc);
-        if (kReadout) ld_row(Cs + rn * kN, Cc);
+        if (kReadout) {
+            // the readout has consumed C(k): refill its slot with C(k+2) after the stores
+            asm volatile("" ::"v"(yv) : "memory");
+            crow(kk + 2, Cr[j & 1]);
+        }
         cur = nxt;
+        // Token boundary: no instruction moves across it. Within a token the next prelude and
+        // this update interleave freely; across tokens the scheduler would hoist preludes ahead
+        // of the loads they wait for.
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     int k = kbeg;
@@ -379,9 +417,10 @@ __global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
 // meet in the middle of the chunk through the park (LDS, or a global scratch region per
 // workgroup when the chunk is long; see the file header).
 template <typename IO, bool kCarry, bool kGlobalPark>
-__global__ __launch_bounds__(128) void k_bidir_scan(ScanArgs a) {
-    extern __shared__ float lds_park[];  // [T][64] when the park is in LDS
+__global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
+    extern __shared__ float lds_parks[];  // [subs][T][64] when the park is in LDS
     const WgCoords c = wg_coords(a);
+    float* lds_park = lds_parks + c.sub * a.T * kWave;
     Lane ln;
     ln.init(a, c.dir, c.dc);
     if (kCarry) {
@@ -407,7 +446,7 @@ __global__ __launch_bounds__(128) void k_bidir_scan(ScanArgs a) {
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
 // from a zero state, and the sum of delta over the chunk.
 template <typename IO>
-__global__ __launch_bounds__(128) void k_chunk_aggregate(ScanArgs a) {
+__global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     const WgCoords c = wg_coords(a);
     Lane ln;
     ln.init(a, c.dir, c.dc);
@@ -455,7 +494,7 @@ __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
 // Host side
 
 struct Plan {
-    int64_t nseq, Lp, T, K, ncb, wgs;
+    int64_t nseq, Lp, T, K, ncb, subs, wgs;
     int kernels;
     bool park_global, widen;
     size_t ws;                                 // total scratch bytes
@@ -509,14 +548,14 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     p->Lp = seg_len > 0 ? seg_len : l->seqlen;
     p->nseq = seg_len > 0 ? l->batch * (l->seqlen / seg_len) : l->batch;
     p->ncb = (l->d_inner + kWave - 1) / kWave;
-    const int64_t lanes = p->nseq * p->ncb;  // workgroups of a single pass
+    const int64_t lanes = p->nseq * p->ncb;  // wave pairs (forward + backward) of a single pass
     int64_t T;
     if (l->chunk_len > 0) {
         T = l->chunk_len;
     } else if ((p->Lp <= kMaxChunk && lanes >= 256) || p->Lp <= 32) {
         T = p->Lp;  // single pass: enough workgroups, or too short to be worth chunking
     } else {
-        // Chunk for parallelism (about 1536 workgroups = 3 waves per SIMD), with at least 32
+        // Chunk for parallelism (about 1536 wave pairs = 3 waves per SIMD), with at least 32
         // tokens per chunk.
         int64_t K = (1536 + lanes - 1) / lanes;
         const int64_t kmin = (p->Lp + kMaxChunk - 1) / kMaxChunk;
@@ -529,14 +568,18 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     if (T > kMaxChunk) T = kMaxChunk;
     p->T = T;
     p->K = (p->Lp + T - 1) / T;
-    p->wgs = p->nseq * p->K * p->ncb;
+    // Four waves per workgroup (two channel blocks x two directions) when there are two channel
+    // blocks: the hardware spreads a 4-wave workgroup over the CU's four SIMDs, where 2-wave
+    // workgroups can leave some SIMDs with twice the waves of others.
+    p->subs = p->ncb >= 2 ? 2 : 1;
+    p->wgs = p->nseq * p->K * ((p->ncb + p->subs - 1) / p->subs);
     p->widen = l->io_dtype == VIMSCAN_BF16;
     p->kernels = (p->K > 1 ? 3 : 1) + (p->widen ? 1 : 0);
     p->park_global = p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
     const size_t f = sizeof(float);
     const size_t carry = p->K > 1 ? static_cast<size_t>(2 * p->nseq * p->K) * kN * l->d_inner * f : 0;
     const size_t dsum = p->K > 1 ? static_cast<size_t>(2 * p->nseq * p->K) * l->d_inner * f : 0;
-    const size_t park = p->park_global ? static_cast<size_t>(p->wgs) * p->T * kWave * f : 0;
+    const size_t park = p->park_global ? static_cast<size_t>(p->wgs) * p->subs * p->T * kWave * f : 0;
     const size_t rows = p->widen ? static_cast<size_t>(4) * l->batch * l->seqlen * kN * f : 0;
     p->off_dsum = round_up(carry, 256);
     p->off_park = round_up(p->off_dsum + dsum, 256);
@@ -554,8 +597,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 template <typename IO, bool kGlobalPark>
 void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
-    const dim3 grid(static_cast<unsigned>(p.wgs)), block(128);
-    const size_t lds = kGlobalPark ? 0 : static_cast<size_t>(p.T) * kWave * sizeof(float);
+    const dim3 grid(static_cast<unsigned>(p.wgs)), block(static_cast<unsigned>(128 * p.subs));
+    const size_t lds = kGlobalPark ? 0 : static_cast<size_t>(p.subs * p.T) * kWave * sizeof(float);
     if (carry) hipLaunchKernelGGL((k_bidir_scan<IO, true, kGlobalPark>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark>), grid, block, lds, s, a);
 }
@@ -567,7 +610,8 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s) {
         hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
     }
     if (p.K > 1) {
-        hipLaunchKernelGGL((k_chunk_aggregate<IO>), dim3(static_cast<unsigned>(p.wgs)), dim3(128), 0, s, a);
+        hipLaunchKernelGGL((k_chunk_aggregate<IO>), dim3(static_cast<unsigned>(p.wgs)),
+                           dim3(static_cast<unsigned>(128 * p.subs)), 0, s, a);
         const dim3 cgrid(static_cast<unsigned>(p.ncb), 4, static_cast<unsigned>(2 * p.nseq));
         hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
@@ -690,6 +734,7 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
     a.T = static_cast<int>(p.T);
     a.K = static_cast<int>(p.K);
     a.ncb = static_cast<int>(p.ncb);
+    a.subs = static_cast<int>(p.subs);
     a.general = (launch->flags & VIMSCAN_FLAG_GENERAL_DECAY) ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(launch->stream);
     rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float>(a, p, s) : launch_all<Bf16>(a, p, s);

@@ -53,7 +53,7 @@ def test_plans_for_the_workloads(lib):
     vim_s = plans["vim_s_b128_l197_d768_bf16"]
     # one pass plus the bf16 -> fp32 row widening
     assert (vim_s["chunks"], vim_s["kernels"], vim_s["park_in_workspace"]) == (1, 2, 1)
-    assert vim_s["workgroups"] == 128 * 12
+    assert vim_s["workgroups"] == 128 * 6     # 4 waves: 2 channel blocks x 2 directions
     park = 128 * 12 * 197 * 64 * 4        # the park: one fp32 per token and lane
     rows = 4 * 128 * 197 * 16 * 4         # B_f, C_f, B_b, C_b widened to fp32
     assert vim_s["workspace_bytes"] == park + rows
@@ -69,7 +69,7 @@ def test_plans_for_the_workloads(lib):
     dsum = 2 * 8 * hi["chunks"] * 768 * 4
     assert hi["workspace_bytes"] == carry + dsum + 4 * 8 * 1025 * 16 * 4
     ti = binding.launch_info(64, 197, 384, 16, 0, "f32")
-    assert ti["kernels"] == 1 and ti["workspace_bytes"] == ti["workgroups"] * 197 * 64 * 4
+    assert ti["kernels"] == 1 and ti["workspace_bytes"] == ti["workgroups"] * 2 * 197 * 64 * 4
     # a forced chunk length is honoured and capped at 256 tokens
     assert binding.launch_info(2, 197, 64, chunk_len=16)["chunks"] == 13
     assert binding.launch_info(1, 1000, 64, chunk_len=5000)["chunk_len"] == 256
