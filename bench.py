@@ -89,6 +89,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=None, help="workload name (default: Vim-S)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-general", action="store_true", help="skip the forced general-decay measurement")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-mebibyte buffer 5 times (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the scan on a single MI355X and has no "
@@ -96,6 +98,15 @@ def main(argv=None):
         return 2
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return 0
     from bidirectional_selective_scan_amd import binding
     from bidirectional_selective_scan_amd.configs import HEADLINE, WORKLOADS
     from bidirectional_selective_scan_amd.inputs import make_workload_inputs

@@ -14,8 +14,10 @@
 //  * One workgroup = one chunk of one sequence x 64 channels, two waves: wave 0 runs the forward
 //    recurrence, wave 1 the backward one, one channel per lane, the 16 states in VGPRs. A token's
 //    B and C rows are the same for every channel of a sequence, so they are wave-uniform: fp32
-//    rows come through the scalar unit into SGPRs (bf16 rows are first widened to fp32 by a
-//    small pre-pass, so the loop spends no scalar instructions unpacking them).
+//    B rows come through the scalar unit into SGPRs (bf16 rows are first widened to fp32 by a
+//    small pre-pass, so the loop spends no scalar instructions unpacking them); C rows are
+//    staged once per workgroup in LDS and read as broadcasts (a wave-uniform vector load would
+//    return the same 64 bytes to every lane through the vector memory path).
 //  * The two directions meet in the middle of the chunk: in the first half each wave parks its
 //    branch output (forward for the first half of the chunk, backward for the second), then
 //    after one barrier each wave finishes its own half, adds the parked output of the other
@@ -91,8 +93,18 @@ __device__ __forceinline__ int xcd_remap(int i, int n) {
 // A chunk's rows of one [token][Di] tensor as a buffer resource: loads take the lane's channel
 // offset from a VGPR and the token row offset from an SGPR, so no per-lane address arithmetic
 // is spent per token. Every offset the kernels form lies inside the range.
+// The address is wave-uniform by construction; passing it through readfirstlane makes that
+// explicit, so the descriptor lands in SGPRs in every kernel variant.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), 0,
+                                             static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
 }
 // Raw loads keep the bits as they are in memory (bf16 zero-extended); widening to fp32 happens
 // where the value is used, so a prefetched load is not waited for until then.
@@ -127,8 +139,7 @@ struct ScanArgs {
     const void* z;
     const void* Bm[2];      // io-dtype rows as passed: [0] forward, [1] backward
     const void* Cm[2];
-    const float* Brow[2];   // fp32 rows the scan reads (the inputs, or their widened copies)
-    const float* Crow[2];
+    const float* Brow[2];   // fp32 B rows the scan reads (the inputs, or their widened copies)
     const float* A[2];
     const float* D[2];
     const float* dtb[2];
@@ -136,7 +147,7 @@ struct ScanArgs {
     float* carry;  // chunked: [dir][seq][chunk][n][Di] states; pass 1 end states / pass 2 inputs
     float* dsum;   // chunked: [dir][seq][chunk][Di] sum of delta over the chunk
     float* parkg;  // park in global memory: [workgroup][T][64] (null: the park is in LDS)
-    float* rows;   // bf16 io: widened rows [B_f, C_f, B_b, C_b][tokens][16]
+    float* rows;   // bf16 io: widened B rows [B_f, B_b][tokens][16]
     int64_t tokens;  // batch * seqlen
     int Lp;        // tokens per independent sequence
     int Di;
@@ -265,8 +276,8 @@ enum WalkMode {
 // VGPR slot token k's row just left. Every prefetch index is clamped into the walk, so every
 // load stays inside the chunk.
 template <typename IO, bool kProg, int kMode, bool kGlobalPark>
-__device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park, int kbeg,
-                                     int kend, float& dsum) {
+__device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
+                                     const float* lds_c, int kbeg, int kend, float& dsum) {
     constexpr int P = 4;
     constexpr uint32_t e = IoTraits<IO>::bytes;
     constexpr bool kReadout = kMode != kAggregate;
@@ -285,8 +296,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const __amdgpu_buffer_rsrc_t rp =
         chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.slot) * a.T * kWave : nullptr,
                    static_cast<uint32_t>(a.T) * kWave * 4);
-    const float* Bs = a.Brow[c.dir] + row0 * kN;
-    const float* Cs = a.Crow[c.dir] + row0 * kN;
+    const float* Bs = uniform_ptr(a.Brow[c.dir] + row0 * kN);
     const uint32_t vo = static_cast<uint32_t>(c.dc) * e;
     const uint32_t vp = static_cast<uint32_t>(c.lane) * 4;
     const int last = kend - 1;
@@ -310,24 +320,22 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
     }
     // B rows (SGPRs) run one token ahead: B(k+1) is consumed by the prelude of token k+1 during
-    // step k. C rows travel as wave-uniform vector loads into a two-slot VGPR ring: C(k) is read
-    // by the readout of step k, after which C(k+2) is requested into its slot.
-    const __amdgpu_buffer_rsrc_t rC = chunk_rsrc(Cs, static_cast<uint32_t>(len) * (kN * 4));
-    auto crow = [&](int k, float (&v)[kN]) {
-        const uint32_t so = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lt(min(k, last)))) * (kN * 4);
+    // step k. C rows come from the chunk's copy in LDS (staged once per workgroup), read as
+    // wave-uniform broadcasts at the start of the step that uses them.
+    float Bn[kN], Cv[kN];
+    ld_row(Bs + lt(kbeg) * kN, Bn);
+    auto lds_row = [&](int k, float (&v)[kN]) {
+        const float4* cp = reinterpret_cast<const float4*>(lds_c + lt(min(k, last)) * kN);
 #pragma unroll
         for (int q = 0; q < kN / 4; ++q) {
-            const auto w = __builtin_amdgcn_raw_buffer_load_b128(rC, 0, so + 16 * q, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[4 * q + i] = __uint_as_float(w[i]);
+            const float4 f = cp[q];
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
         }
     };
-    float Bn[kN], Cr[2][kN];
-    ld_row(Bs + lt(kbeg) * kN, Bn);
-    if (kReadout) {
-        crow(kbeg, Cr[0]);
-        crow(kbeg + 1, Cr[1]);
-    }
+    if (kReadout) lds_row(kbeg, Cv);
     Prelude cur = ln.template prelude<kProg>(widen(IO{}, xr[0]), widen(IO{}, dr[0]), Bn);
     ld_row(Bs + lt(min(kbeg + 1, last)) * kN, Bn);
     {
@@ -339,6 +347,8 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     auto body = [&](int kk, int j) {
         const int jn = (j + 1) % P;
         const int tl = lt(kk);
+        float Cn[kN];  // next token's C row, read from LDS a step ahead of its use
+        if (kReadout) lds_row(kk + 1, Cn);
         // Consume the ring slots before refilling them: the empty asm takes the widened values
         // and orders every load after it, so a refill can reuse its slot's register and the loop
         // needs no register copies (a copy would wait for the load just issued).
@@ -363,7 +373,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         const Prelude nxt = ln.template prelude<kProg>(xn, dn, Bn);
         ld_row(Bs + lt(min(kk + 2, last)) * kN, Bn);
         if (kMode == kAggregate) dsum += cur.delta;
-        const float yv = ln.template update<kReadout>(cur, Cr[j & 1]);
+        const float yv = ln.template update<kReadout>(cur, Cv);
         if (kMode == kPark) {
             if (kGlobalPark)
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), rp, vp,
@@ -375,12 +385,11 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             const float other = kGlobalPark ? pv : lds_park[tl * kWave + c.lane];
             if (c.valid) st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (yv + other));
         }
-        if (kReadout) {
-            // the readout has consumed C(k): refill its slot with C(k+2) after the stores
-            asm volatile("" ::"v"(yv) : "memory");
-            crow(kk + 2, Cr[j & 1]);
-        }
         cur = nxt;
+        if (kReadout) {
+#pragma unroll
+            for (int n = 0; n < kN; ++n) Cv[n] = Cn[n];
+        }
         // Token boundary: no instruction moves across it. Within a token the next prelude and
         // this update interleave freely; across tokens the scheduler would hoist preludes ahead
         // of the loads they wait for.
@@ -397,20 +406,58 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         if (k + j < kend) body(k + j, j);
 }
 
-// Widen the bf16 B/C rows to fp32 rows once per call: [B_f, C_f, B_b, C_b][tokens][16].
-// One thread per 32-bit word (two bf16 values).
+// Widen the bf16 B rows to fp32 rows once per call: [B_f, B_b][tokens][16], read through the
+// scalar unit by the scan. One thread per 32-bit word (two bf16 values).
 __global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
     const int64_t words = a.tokens * (kN / 2);
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= 4 * words) return;
-    const int which = static_cast<int>(i / words);  // 0 B_f, 1 C_f, 2 B_b, 3 C_b
+    if (i >= 2 * words) return;
+    const int which = static_cast<int>(i / words);  // 0 B_f, 1 B_b
     const int64_t w = i - which * words;
-    const void* src = which == 0 ? a.Bm[0] : which == 1 ? a.Cm[0] : which == 2 ? a.Bm[1] : a.Cm[1];
-    const uint32_t u = static_cast<const uint32_t*>(src)[w];
+    const uint32_t u = static_cast<const uint32_t*>(a.Bm[which])[w];
     float2 f;
     f.x = __uint_as_float(u << 16);
     f.y = __uint_as_float(u & 0xffff0000u);
     reinterpret_cast<float2*>(a.rows + which * a.tokens * kN)[w] = f;
+}
+
+// Copy the chunk's C rows of both directions into LDS as fp32: lds_c[dir][t][16], t in [0, len).
+// Each direction's rows are one contiguous range of 32-bit words in memory; every thread issues
+// all its loads before widening and storing, so the copy costs one memory round trip.
+template <typename IO>
+__device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& c, float* lds_c) {
+    constexpr int kU = 16;                                     // words per thread per pass
+    constexpr int kPerWord = 4 / IoTraits<IO>::bytes;          // values per 32-bit word
+    const int len = c.t1 - c.t0;
+    const int64_t row0 = static_cast<int64_t>(c.seq) * a.Lp + c.t0;
+    const int wpd = len * kN / kPerWord;                       // words per direction
+    const uint32_t* src0 = reinterpret_cast<const uint32_t*>(
+        static_cast<const typename IoTraits<IO>::elem*>(a.Cm[0]) + row0 * kN);
+    const uint32_t* src1 = reinterpret_cast<const uint32_t*>(
+        static_cast<const typename IoTraits<IO>::elem*>(a.Cm[1]) + row0 * kN);
+    const int nt = static_cast<int>(blockDim.x);
+    for (int base = static_cast<int>(threadIdx.x); base < 2 * wpd; base += kU * nt) {
+        uint32_t w[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = base + u * nt;
+            w[u] = i < wpd ? src0[i] : (i < 2 * wpd ? src1[i - wpd] : 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = base + u * nt;
+            if (i < 2 * wpd) {
+                const int dir = i >= wpd ? 1 : 0;
+                float* dst = lds_c + dir * a.T * kN + (i - dir * wpd) * kPerWord;
+                if (kPerWord == 1) {
+                    dst[0] = __uint_as_float(w[u]);
+                } else {
+                    dst[0] = __uint_as_float(w[u] << 16);
+                    dst[1] = __uint_as_float(w[u] & 0xffff0000u);
+                }
+            }
+        }
+    }
 }
 
 // Main scan: one chunk of one sequence, 64 channels; wave 0 forward, wave 1 backward. The waves
@@ -418,9 +465,11 @@ __global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
 // workgroup when the chunk is long; see the file header).
 template <typename IO, bool kCarry, bool kGlobalPark>
 __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
-    extern __shared__ float lds_parks[];  // [subs][T][64] when the park is in LDS
+    extern __shared__ float lds[];  // C rows [2][T][16], then the park [subs][T][64] when in LDS
     const WgCoords c = wg_coords(a);
-    float* lds_park = lds_parks + c.sub * a.T * kWave;
+    float* lds_c = lds + c.dir * a.T * kN;
+    float* lds_park = lds + 2 * a.T * kN + c.sub * a.T * kWave;
+    stage_c_rows<IO>(a, c, lds);
     Lane ln;
     ln.init(a, c.dir, c.dc);
     if (kCarry) {
@@ -436,11 +485,12 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     const int half = len >> 1;
     const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
     float unused = 0.0f;
-    if (prog) walk<IO, true, kPark, kGlobalPark>(a, c, ln, lds_park, 0, n1, unused);
-    else walk<IO, false, kPark, kGlobalPark>(a, c, ln, lds_park, 0, n1, unused);
+    __syncthreads();  // the C rows are staged
+    if (prog) walk<IO, true, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
+    else walk<IO, false, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
-    if (prog) walk<IO, true, kFinish, kGlobalPark>(a, c, ln, lds_park, n1, len, unused);
-    else walk<IO, false, kFinish, kGlobalPark>(a, c, ln, lds_park, n1, len, unused);
+    if (prog) walk<IO, true, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
+    else walk<IO, false, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
@@ -454,8 +504,8 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
     const bool prog = !a.general && __all(ln.is_progression(a, c.dir, c.dc));
     float s = 0.0f;
-    if (prog) walk<IO, true, kAggregate, false>(a, c, ln, nullptr, 0, c.t1 - c.t0, s);
-    else walk<IO, false, kAggregate, false>(a, c, ln, nullptr, 0, c.t1 - c.t0, s);
+    if (prog) walk<IO, true, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, c.t1 - c.t0, s);
+    else walk<IO, false, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, c.t1 - c.t0, s);
     if (c.valid) {
         const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
         float* dst = a.carry + slot * kN * a.Di;
@@ -580,7 +630,7 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     const size_t carry = p->K > 1 ? static_cast<size_t>(2 * p->nseq * p->K) * kN * l->d_inner * f : 0;
     const size_t dsum = p->K > 1 ? static_cast<size_t>(2 * p->nseq * p->K) * l->d_inner * f : 0;
     const size_t park = p->park_global ? static_cast<size_t>(p->wgs) * p->subs * p->T * kWave * f : 0;
-    const size_t rows = p->widen ? static_cast<size_t>(4) * l->batch * l->seqlen * kN * f : 0;
+    const size_t rows = p->widen ? static_cast<size_t>(2) * l->batch * l->seqlen * kN * f : 0;
     p->off_dsum = round_up(carry, 256);
     p->off_park = round_up(p->off_dsum + dsum, 256);
     p->off_rows = round_up(p->off_park + park, 256);
@@ -598,7 +648,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 template <typename IO, bool kGlobalPark>
 void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
     const dim3 grid(static_cast<unsigned>(p.wgs)), block(static_cast<unsigned>(128 * p.subs));
-    const size_t lds = kGlobalPark ? 0 : static_cast<size_t>(p.subs * p.T) * kWave * sizeof(float);
+    const size_t lds = (2 * p.T * kN + (kGlobalPark ? 0 : p.subs * p.T * kWave)) * sizeof(float);
     if (carry) hipLaunchKernelGGL((k_bidir_scan<IO, true, kGlobalPark>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark>), grid, block, lds, s, a);
 }
@@ -606,7 +656,7 @@ void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
 template <typename IO>
 int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s) {
     if (p.widen) {
-        const int64_t threads = a.tokens * (kN / 2) * 4;
+        const int64_t threads = a.tokens * (kN / 2) * 2;
         hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
     }
     if (p.K > 1) {
@@ -718,15 +768,11 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
     a.rows = p.widen ? reinterpret_cast<float*>(ws + p.off_rows) : nullptr;
     a.tokens = launch->batch * launch->seqlen;
     if (p.widen) {
-        for (int i = 0; i < 2; ++i) {
-            a.Brow[i] = a.rows + (2 * i) * a.tokens * kN;
-            a.Crow[i] = a.rows + (2 * i + 1) * a.tokens * kN;
-        }
+        a.Brow[0] = a.rows;
+        a.Brow[1] = a.rows + a.tokens * kN;
     } else {
         a.Brow[0] = static_cast<const float*>(B_f);
         a.Brow[1] = static_cast<const float*>(B_b);
-        a.Crow[0] = static_cast<const float*>(C_f);
-        a.Crow[1] = static_cast<const float*>(C_b);
     }
     a.Lp = static_cast<int>(p.Lp);
     a.Di = static_cast<int>(launch->d_inner);

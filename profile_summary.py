@@ -1,0 +1,105 @@
+"""Summaries of rocprofv3 output for profiles/.
+
+  python profile_summary.py trace --stats <run_kernel_stats.csv> --cmd "<command>" --out profiles/<name>.txt
+      per-kernel call count and average / min / max duration from a --kernel-trace --stats run.
+
+  python profile_summary.py traffic --fetch <fetch counter csv> --write <write counter csv>
+      --calib-fetch <csv> --calib-write <csv> --calib-bytes N --kernel <substring>
+      --workload <name> --source <kernel source file> --cmd "<commands>" --out profiles/<name>.json
+      HBM traffic per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+      each scaled by what the same counter reads for a plain copy of N bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import statistics
+
+
+def kernel_stats(path):
+    rows = list(csv.DictReader(open(path)))
+    return rows
+
+
+def counter_per_dispatch(path, kernel_substr, counter):
+    """Mean over dispatches of ``counter`` for kernels whose name contains kernel_substr."""
+    per = collections.defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {path}")
+    return statistics.mean(per.values()), len(per)
+
+
+def largest_kernel_counter(path, counter):
+    """Counter value (per dispatch, mean) of the kernel with the largest value: the copy kernel of a
+    calibration run."""
+    per = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    top = max(per.values())
+    picked = [v for v in per.values() if v > 0.5 * top]
+    return statistics.mean(picked), names[max(per, key=per.get)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--stats", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--out", required=True)
+    f = sub.add_parser("traffic")
+    for k in ("fetch", "write", "calib_fetch", "calib_write", "kernel", "workload", "source", "cmd", "out"):
+        f.add_argument("--" + k.replace("_", "-"), required=True)
+    f.add_argument("--calib-bytes", type=int, required=True)
+    a = ap.parse_args()
+
+    if a.what == "trace":
+        rows = kernel_stats(a.stats)
+        lines = [f"command: {a.cmd}", "",
+                 f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share':>7s}"]
+        for r in rows:
+            name = r["Name"]
+            short = name if len(name) <= 70 else name[:67] + "..."
+            lines.append(f"{short:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} "
+                         f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
+                         f"{float(r['Percentage']):6.2f}%")
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
+
+    fetch_kib, n1 = counter_per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
+    write_kib, n2 = counter_per_dispatch(a.write, a.kernel, "WRITE_SIZE")
+    cf_kib, cf_name = largest_kernel_counter(a.calib_fetch, "FETCH_SIZE")
+    cw_kib, cw_name = largest_kernel_counter(a.calib_write, "WRITE_SIZE")
+    f_scale = a.calib_bytes / (cf_kib * 1024.0)
+    w_scale = a.calib_bytes / (cw_kib * 1024.0)
+    rec = {
+        "workload": a.workload,
+        "kernel": a.kernel,
+        "kernel_source_sha256_16": hashlib.sha256(open(a.source, "rb").read()).hexdigest()[:16],
+        "fetch_kib_per_dispatch": round(fetch_kib, 1),
+        "write_kib_per_dispatch": round(write_kib, 1),
+        "dispatches": [n1, n2],
+        "calibration": {"bytes": a.calib_bytes, "fetch_kib": round(cf_kib, 1), "write_kib": round(cw_kib, 1),
+                        "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                        "copy_kernel": cf_name[:80]},
+        "fetch_bytes_per_launch": int(fetch_kib * 1024 * f_scale),
+        "write_bytes_per_launch": int(write_kib * 1024 * w_scale),
+        "bytes_per_launch": int(fetch_kib * 1024 * f_scale + write_kib * 1024 * w_scale),
+        "command": a.cmd,
+    }
+    json.dump(rec, open(a.out, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()
