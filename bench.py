@@ -32,20 +32,24 @@ CACHE_BYTES = 256 * 2 ** 20   # Infinity Cache
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_vim_s.json")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_selective_scan_amd", "csrc", "vimscan.hip")
 
-# ALU work of the scan per (batch, token, channel), in fp32 VALU issue slots (an FMA, multiply or
-# add is one slot per lane; a transcendental is four: CDNA issues exp2/log2/rcp at a quarter of
-# the FMA rate and the two do not overlap). Counts follow the arithmetic of the path taken:
-#   per direction: softplus (exp, log + 3 ops), u = delta*x, D*x, and per state n:
-#     general: delta*A, exp, h*Abar, h += u*B, y += C*h        -> 4 ops + 1 transcendental
-#     progression: Abar_n = Abar_{n-2} * q^2 (and e0, e1),     -> 4 ops per n + 2 exps per token
-#   combine: yf + yb, silu (exp, rcp + 2 ops), product          -> 4 ops + 2 transcendentals
+# ALU work of the scan per (batch, token, channel), in fp32 VALU issue slots: an FMA, multiply,
+# add, compare or select is one slot per lane; a transcendental (exp2, log2, rcp) is four, since
+# CDNA issues them at a quarter of the FMA rate and they do not overlap with it. Per direction:
+#   softplus: v*log2e, exp2, +1, log2, *ln2, compare, select       5 ops + 2 transcendentals
+#   u = delta*x, D*x                                                2 ops
+#   transitions exp(delta*A[n]), 16 states:
+#     general: 16 x (delta*A, exp2)                                16 ops + 16 transcendentals
+#     arithmetic progression: delta*a0, delta*da, 2 exp2,
+#                             q^2, q^4, 15 products                19 ops + 2 transcendentals
+#   delta*x*B[n]: 16 multiplies; state h = h*e + ub: 16 FMAs; readout 16 FMAs + 3 adds
+# Combine: yf + yb, silu (-z*log2e, exp2, +1, rcp, *z), product    5 ops + 2 transcendentals
 TRANS_SLOTS = 4
 
 
 def alu_slots_per_element(progression: bool) -> float:
-    per_dir_ops = 3 + 2 + (16 * 4)
+    per_dir_ops = 5 + 2 + (19 if progression else 16) + 16 + 16 + 19
     per_dir_trans = 2 + (2 if progression else 16)
-    ops = 2 * per_dir_ops + 4
+    ops = 2 * per_dir_ops + 5
     trans = 2 * per_dir_trans + 2
     return ops + TRANS_SLOTS * trans
 
