@@ -166,6 +166,9 @@ struct Prelude {
     float ub[kN];        // inputs delta * x * B[n]
 };
 
+// How a wave forms its 16 transitions (see Lane::prelude).
+enum Decay { kGeneral = 0, kProgression = 1, kGeometric = 2 };
+
 // Per-lane recurrence state of one direction over one channel.
 struct Lane {
     float h[kN];
@@ -193,7 +196,17 @@ struct Lane {
         return ok;
     }
 
-    template <bool kProgression>
+    // The transition form this wave uses: one form for all 64 lanes (a wave-wide vote).
+    __device__ __forceinline__ int decay_form(const ScanArgs& a, int dir, int dc) const {
+        if (a.general) return kGeneral;
+        if (!__all(is_progression(a, dir, dc))) return kGeneral;
+        return __all(a0 == da) ? kGeometric : kProgression;
+    }
+
+    // Transition forms: kGeneral takes one exponential per state; kProgression uses
+    // exp(delta*A0) * q^n for a row A0 + n*dA; kGeometric is the progression with A0 == dA, where
+    // the transitions are q^(n+1) and the first exponential is q itself.
+    template <int kDecay>
     __device__ __forceinline__ Prelude prelude(float xv, float dtv, const float (&Bv)[kN]) const {
         Prelude p;
         p.delta = softplus(dtv + bias);
@@ -201,20 +214,27 @@ struct Lane {
         p.dx = Dd * xv;
 #pragma unroll
         for (int n = 0; n < kN; ++n) p.ub[n] = u * Bv[n];
-        if (kProgression) {
+        if (kDecay == kGeneral) {
+#pragma unroll
+            for (int n = 0; n < kN; ++n) p.e[n] = fast_exp2(p.delta * a2[n]);
+        } else {
             // e[n] = e0 * q^n along four independent chains of stride q^4
             const float q = fast_exp2(p.delta * da);
             const float q2 = q * q;
             const float q4 = q2 * q2;
-            p.e[0] = fast_exp2(p.delta * a0);
-            p.e[1] = p.e[0] * q;
-            p.e[2] = p.e[0] * q2;
-            p.e[3] = p.e[1] * q2;
+            if (kDecay == kGeometric) {
+                p.e[0] = q;
+                p.e[1] = q2;
+                p.e[2] = q2 * q;
+                p.e[3] = q4;
+            } else {
+                p.e[0] = fast_exp2(p.delta * a0);
+                p.e[1] = p.e[0] * q;
+                p.e[2] = p.e[0] * q2;
+                p.e[3] = p.e[1] * q2;
+            }
 #pragma unroll
             for (int n = 4; n < kN; ++n) p.e[n] = p.e[n - 4] * q4;
-        } else {
-#pragma unroll
-            for (int n = 0; n < kN; ++n) p.e[n] = fast_exp2(p.delta * a2[n]);
         }
         return p;
     }
@@ -251,7 +271,7 @@ __device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a) {
     c.dir = wave & 1;
     c.sub = wave >> 1;
     c.slot = lid * a.subs + c.sub;  // this wave pair's park region
-    c.cb = cbw * a.subs + c.sub;    // may be past the last block when ncb is odd: no lane stores
+    c.cb = cbw * a.subs + c.sub;    // may be past the last block when ncb is odd: y gets no stores
     c.d = c.cb * kWave + c.lane;
     c.valid = c.d < a.Di;
     c.dc = c.valid ? c.d : a.Di - 1;
@@ -275,7 +295,7 @@ enum WalkMode {
 // run on the prelude formed a step earlier; then the C row of token k+2 is requested into the
 // VGPR slot token k's row just left. Every prefetch index is clamped into the walk, so every
 // load stays inside the chunk.
-template <typename IO, bool kProg, int kMode, bool kGlobalPark>
+template <typename IO, int kDecay, int kMode, bool kGlobalPark>
 __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
                                      const float* lds_c, int kbeg, int kend, float& dsum) {
     constexpr int P = 4;
@@ -292,7 +312,9 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const __amdgpu_buffer_rsrc_t rx = chunk_rsrc(static_cast<const E*>(a.x) + eoff, span);
     const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(static_cast<const E*>(a.dt) + eoff, span);
     const __amdgpu_buffer_rsrc_t rz = chunk_rsrc(static_cast<const E*>(a.z) + eoff, span);
-    const __amdgpu_buffer_rsrc_t ry = chunk_rsrc(static_cast<E*>(a.y) + eoff, span);
+    // A wave whose channel block lies past the last one (the spare half of the last workgroup
+    // when the number of blocks is odd) gets an empty y range: the hardware drops its stores.
+    const __amdgpu_buffer_rsrc_t ry = chunk_rsrc(static_cast<E*>(a.y) + eoff, c.cb < a.ncb ? span : 0u);
     const __amdgpu_buffer_rsrc_t rp =
         chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.slot) * a.T * kWave : nullptr,
                    static_cast<uint32_t>(a.T) * kWave * 4);
@@ -336,7 +358,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
     };
     if (kReadout) lds_row(kbeg, Cv);
-    Prelude cur = ln.template prelude<kProg>(widen(IO{}, xr[0]), widen(IO{}, dr[0]), Bn);
+    Prelude cur = ln.template prelude<kDecay>(widen(IO{}, xr[0]), widen(IO{}, dr[0]), Bn);
     ld_row(Bs + lt(min(kbeg + 1, last)) * kN, Bn);
     {
         const uint32_t so = toff(kbeg + P);
@@ -370,7 +392,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             if (kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
         // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
-        const Prelude nxt = ln.template prelude<kProg>(xn, dn, Bn);
+        const Prelude nxt = ln.template prelude<kDecay>(xn, dn, Bn);
         ld_row(Bs + lt(min(kk + 2, last)) * kN, Bn);
         if (kMode == kAggregate) dsum += cur.delta;
         const float yv = ln.template update<kReadout>(cur, Cv);
@@ -383,7 +405,12 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
         if (kMode == kFinish) {
             const float other = kGlobalPark ? pv : lds_park[tl * kWave + c.lane];
-            if (c.valid) st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (yv + other));
+            // No branch on c.valid: a lane past d_inner in the last block runs channel
+            // d_inner-1 on the same inputs and parameters, in the same wave (so with the same
+            // transition form), and stores the same bits to the same element. Without the branch
+            // the readout stays in the token's single basic block, where it interleaves with the
+            // next token's prelude.
+            st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (yv + other));
         }
         cur = nxt;
         if (kReadout) {
@@ -480,17 +507,19 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
     }
-    const bool prog = !a.general && __all(ln.is_progression(a, c.dir, c.dc));
+    const int form = ln.decay_form(a, c.dir, c.dc);
     const int len = c.t1 - c.t0;
     const int half = len >> 1;
     const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
     float unused = 0.0f;
     __syncthreads();  // the C rows are staged
-    if (prog) walk<IO, true, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
-    else walk<IO, false, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
+    if (form == kGeometric) walk<IO, kGeometric, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
+    else if (form == kProgression) walk<IO, kProgression, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
+    else walk<IO, kGeneral, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
-    if (prog) walk<IO, true, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
-    else walk<IO, false, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
+    if (form == kGeometric) walk<IO, kGeometric, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
+    else if (form == kProgression) walk<IO, kProgression, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
+    else walk<IO, kGeneral, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
@@ -502,10 +531,12 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     ln.init(a, c.dir, c.dc);
 #pragma unroll
     for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
-    const bool prog = !a.general && __all(ln.is_progression(a, c.dir, c.dc));
+    const int form = ln.decay_form(a, c.dir, c.dc);
+    const int len = c.t1 - c.t0;
     float s = 0.0f;
-    if (prog) walk<IO, true, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, c.t1 - c.t0, s);
-    else walk<IO, false, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, c.t1 - c.t0, s);
+    if (form == kGeometric) walk<IO, kGeometric, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, len, s);
+    else if (form == kProgression) walk<IO, kProgression, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, len, s);
+    else walk<IO, kGeneral, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, len, s);
     if (c.valid) {
         const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
         float* dst = a.carry + slot * kN * a.Di;

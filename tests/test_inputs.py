@@ -5,7 +5,7 @@ import torch
 
 from bidirectional_selective_scan_amd.configs import WORKLOADS
 from bidirectional_selective_scan_amd.inputs import (bf16_bits_to_f32, f32_to_bf16_bits, make_inputs,
-                                                     round_to_io)
+                                                     progression_params, round_to_io)
 
 
 def test_deterministic_and_seed_dependent():
@@ -56,3 +56,16 @@ def test_workload_table():
     assert vim_s.algorithmic_bytes() == 158_265_344
     folded = WORKLOADS[4]
     assert folded.seqlen == 256 * 51 and folded.seg_len == 51
+
+
+def test_progression_params_are_exact_progressions():
+    p = progression_params(200, 16, 5)
+    n = np.arange(16, dtype=np.float32)
+    for sfx in ("f", "b"):
+        A = p["A_" + sfx]
+        s = (A[:, 1] - A[:, 0]).astype(np.float32)
+        assert np.array_equal(A, (A[:, :1] + n[None, :] * s[:, None]).astype(np.float32))
+        assert (A < 0).all()
+        geometric = A[:, 1] == 2 * A[:, 0]
+        assert geometric[64:128].all() and geometric[192:].all()
+        assert not geometric[:64].all()

@@ -9,16 +9,22 @@ import torch
 import oracle
 from bidirectional_selective_scan_amd import binding
 from bidirectional_selective_scan_amd.configs import WORKLOADS
-from bidirectional_selective_scan_amd.inputs import make_inputs, make_workload_inputs, random_params
+from bidirectional_selective_scan_amd.inputs import (make_inputs, make_workload_inputs, progression_params,
+                                                     random_params)
 from gpu_helpers import assert_close, run_gpu, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
 
-def _case(B, L, Di, io, seed, random=False):
+def _case(B, L, Di, io, seed, params="s4d"):
+    """Inputs of the default recipe; params: "s4d" keeps A[d, n] = -(n+1) (every wave takes the
+    geometric transitions), "random" draws A freely (general transitions), "progression" gives
+    exact arithmetic-progression rows (alternate 64-channel blocks geometric / progression)."""
     inp = make_inputs(B, L, Di, 16, io, seed)
-    if random:
+    if params == "random":
         inp.update(random_params(Di, 16, seed + 7))
+    elif params == "progression":
+        inp.update(progression_params(Di, 16, seed + 7))
     return inp
 
 
@@ -60,20 +66,20 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("random", [False, True], ids=["s4d_A", "random_A"])
+@pytest.mark.parametrize("params", ["s4d", "random", "progression"], ids=lambda p: p + "_A")
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%d_L%d_D%d_seg%d_chunk%d" % s)
-def test_shapes(shape, random, io):
+def test_shapes(shape, params, io):
     B, L, Di, seg, chunk = shape
-    inp = _case(B, L, Di, io, seed=L * 31 + Di, random=random)
+    inp = _case(B, L, Di, io, seed=L * 31 + Di, params=params)
     dev = to_device(inp, io)
     y = to_f64(run_gpu(dev, seg_len=seg, chunk_len=chunk))
     ref = oracle.bidir_fwd(inp, seg_len=seg)
-    assert_close(y, ref, io, f"{shape} random={random}")
+    assert_close(y, ref, io, f"{shape} params={params}")
 
 
 def test_direction_parameters_are_routed():
     """Forward and backward parameters differ (A, D, dt_bias, B, C): a swap on the GPU fails."""
-    inp = _case(2, 97, 128, "f32", seed=3, random=True)
+    inp = _case(2, 97, 128, "f32", seed=3, params="random")
     dev = to_device(inp, "f32")
     y = to_f64(run_gpu(dev))
     assert_close(y, oracle.bidir_fwd(inp), "f32", "routed")
