@@ -31,7 +31,8 @@ class _Launch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("d_inner", ctypes.c_int64),
                 ("d_state", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("chunk_len", ctypes.c_int64), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+                ("scan_events", ctypes.c_void_p * 2)]
 
 
 class _Plan(ctypes.Structure):
@@ -160,6 +161,12 @@ class PreparedCall:
         self._launch = launch
         self._fn = lib.vimscan_bidir_fwd
         self._args = tuple(t.data_ptr() for t in ios + params) + (int(seg_len), out.data_ptr(), ctypes.byref(launch))
+
+    def set_scan_events(self, ev0: int = 0, ev1: int = 0):
+        """hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event, already created) that the
+        following calls record just before and just after the main scan kernel; 0, 0 stops it."""
+        self._launch.scan_events[0] = ev0 or None
+        self._launch.scan_events[1] = ev1 or None
 
     def __call__(self):
         _check(self._fn(*self._args))

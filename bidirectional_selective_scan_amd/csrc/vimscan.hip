@@ -33,12 +33,13 @@
 //    combine kernel folds these left-to-right (forward) and right-to-left (backward) into the
 //    state entering every chunk; pass 2 re-runs each chunk from its incoming state with the
 //    readout. Carries live in the caller's workspace.
-//  * Transitions use the hardware exp2 with A pre-scaled by log2(e). When a channel's A row is
-//    an arithmetic progression in n (as the S4D-real initialisation A[d,n] = -(n+1) is), the
-//    16 transitions are exp(delta*A0) * q^n with q = exp(delta*dA): two exponentials and
-//    multiplies instead of 16 exponentials (the transcendental unit issues at a quarter of the
-//    FMA rate). A wave takes that path only when every lane's row qualifies;
-//    VIMSCAN_FLAG_GENERAL_DECAY turns it off.
+//  * delta is kept in log2 units (softplus * log2 e), so the transitions are the hardware exp2
+//    of delta2 * A; the state is then scaled by log2(e), which the C rows undo (they are staged
+//    as C * ln 2). When a channel's A row is an arithmetic progression in n, the 16 transitions
+//    are exp(delta*A0) * q^n with q = exp(delta*dA): two exponentials (one when A0 == dA, as in
+//    the S4D-real initialisation A[d,n] = -(n+1)) and multiplies instead of 16 exponentials
+//    (the transcendental unit issues at a quarter of the FMA rate). A wave takes that path
+//    only when every lane's row qualifies; VIMSCAN_FLAG_GENERAL_DECAY turns it off.
 //  * Workgroup ids are remapped so that consecutive logical workgroups (which share a
 //    sequence's B/C rows) land on the same XCD and its L2.
 
@@ -73,10 +74,15 @@ __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
-// softplus(v) = ln(1 + e^v); above 20 the correction log1p(e^-v) < 2.1e-9 and v is returned.
-__device__ __forceinline__ float softplus(float v) {
-    const float r = kLn2 * fast_log2(1.0f + fast_exp2(v * kLog2e));
-    return v > 20.0f ? v : r;
+// softplus(v) * log2(e) = log2(1 + 2^(v log2 e)). The scan keeps delta in these log2 units: the
+// transitions are then 2^(A * delta2) with A as given, and the conversion back to natural units
+// is folded into the C rows (C * ln 2, applied once when they are staged). Above v = 20 the
+// correction log2(1 + 2^-(v log2 e)) < 3e-9 and v log2 e is returned.
+// Takes dt and bias * log2(e), so v * log2(e) is one fma.
+__device__ __forceinline__ float softplus_log2(float dt, float bias2) {
+    const float vl = fmaf(dt, kLog2e, bias2);
+    const float r = fast_log2(1.0f + fast_exp2(vl));
+    return vl > 20.0f * kLog2e ? vl : r;
 }
 
 // silu(v) = v / (1 + e^-v)
@@ -126,9 +132,11 @@ __device__ __forceinline__ void st_buf(Bf16, __amdgpu_buffer_rsrc_t r, uint32_t 
 
 // One token's fp32 B or C row (16 values), read through the scalar unit: the row address is
 // wave-uniform and the constant address space makes the compiler emit scalar loads.
+// The row is given as a base and a 32-bit byte offset, which the scalar load takes as its
+// offset operand (no 64-bit address arithmetic per row).
 typedef const float __attribute__((address_space(4)))* ConstRow;
-__device__ __forceinline__ void ld_row(const float* row, float (&v)[kN]) {
-    const ConstRow p = (ConstRow)(row);
+__device__ __forceinline__ void ld_row(const float* base, uint32_t off, float (&v)[kN]) {
+    const ConstRow p = (ConstRow)(reinterpret_cast<const char*>(base) + off);
 #pragma unroll
     for (int n = 0; n < kN; ++n) v[n] = p[n];
 }
@@ -144,8 +152,8 @@ struct ScanArgs {
     const float* D[2];
     const float* dtb[2];
     void* y;
-    float* carry;  // chunked: [dir][seq][chunk][n][Di] states; pass 1 end states / pass 2 inputs
-    float* dsum;   // chunked: [dir][seq][chunk][Di] sum of delta over the chunk
+    float* carry;  // chunked: [dir][seq][chunk][n][Di] states (x log2 e); pass 1 end states / pass 2 inputs
+    float* dsum;   // chunked: [dir][seq][chunk][Di] sum of delta * log2(e) over the chunk
     float* parkg;  // park in global memory: [workgroup][T][64] (null: the park is in LDS)
     float* rows;   // bf16 io: widened B rows [B_f, B_b][tokens][16]
     int64_t tokens;  // batch * seqlen
@@ -161,9 +169,9 @@ struct ScanArgs {
 
 // The state-independent part of one token, computed a token ahead of its state update.
 struct Prelude {
-    float delta, dx;     // softplus(dt + bias), D*x
-    float e[kN];         // transitions exp(delta * A[d, n])
-    float ub[kN];        // inputs delta * x * B[n]
+    float delta2, x;     // softplus(dt + bias) * log2(e); x (for the skip term)
+    float e[kN];         // transitions exp(delta * A[d, n]) = 2^(delta2 * A[d, n])
+    float ub[kN];        // inputs delta2 * x * B[n] (the state is kept scaled by log2(e))
 };
 
 // How a wave forms its 16 transitions (see Lane::prelude).
@@ -171,19 +179,19 @@ enum Decay { kGeneral = 0, kProgression = 1, kGeometric = 2 };
 
 // Per-lane recurrence state of one direction over one channel.
 struct Lane {
-    float h[kN];
-    float a2[kN];   // A[d, n] * log2(e)
-    float a0, da;   // arithmetic progression: A[d,0]*log2(e), (A[d,1]-A[d,0])*log2(e)
-    float Dd, bias;
+    float h[kN];    // state scaled by log2(e)
+    float an[kN];   // A[d, n]
+    float a0, da;   // arithmetic progression: A[d,0], A[d,1]-A[d,0]
+    float Dsum, bias2;  // D_f[d] + D_b[d] (the skip terms of both directions); dt_bias[d] * log2(e)
 
     __device__ __forceinline__ void init(const ScanArgs& a, int dir, int dc) {
         const float* A = a.A[dir];
 #pragma unroll
-        for (int n = 0; n < kN; ++n) a2[n] = A[dc * kN + n] * kLog2e;
-        a0 = A[dc * kN] * kLog2e;
-        da = (A[dc * kN + 1] - A[dc * kN]) * kLog2e;
-        Dd = a.D[dir][dc];
-        bias = a.dtb[dir][dc];
+        for (int n = 0; n < kN; ++n) an[n] = A[dc * kN + n];
+        a0 = A[dc * kN];
+        da = A[dc * kN + 1] - A[dc * kN];
+        Dsum = a.D[0][dc] + a.D[1][dc];
+        bias2 = a.dtb[dir][dc] * kLog2e;
     }
 
     // True when A[d, :] is exactly A0 + n*(A1 - A0) in fp32.
@@ -209,17 +217,17 @@ struct Lane {
     template <int kDecay>
     __device__ __forceinline__ Prelude prelude(float xv, float dtv, const float (&Bv)[kN]) const {
         Prelude p;
-        p.delta = softplus(dtv + bias);
-        const float u = p.delta * xv;
-        p.dx = Dd * xv;
+        p.delta2 = softplus_log2(dtv, bias2);
+        const float u = p.delta2 * xv;
+        p.x = xv;
 #pragma unroll
         for (int n = 0; n < kN; ++n) p.ub[n] = u * Bv[n];
         if (kDecay == kGeneral) {
 #pragma unroll
-            for (int n = 0; n < kN; ++n) p.e[n] = fast_exp2(p.delta * a2[n]);
+            for (int n = 0; n < kN; ++n) p.e[n] = fast_exp2(p.delta2 * an[n]);
         } else {
             // e[n] = e0 * q^n along four independent chains of stride q^4
-            const float q = fast_exp2(p.delta * da);
+            const float q = fast_exp2(p.delta2 * da);
             const float q2 = q * q;
             const float q4 = q2 * q2;
             if (kDecay == kGeometric) {
@@ -228,7 +236,7 @@ struct Lane {
                 p.e[2] = q2 * q;
                 p.e[3] = q4;
             } else {
-                p.e[0] = fast_exp2(p.delta * a0);
+                p.e[0] = fast_exp2(p.delta2 * a0);
                 p.e[1] = p.e[0] * q;
                 p.e[2] = p.e[0] * q2;
                 p.e[3] = p.e[1] * q2;
@@ -239,16 +247,18 @@ struct Lane {
         return p;
     }
 
-    // State update h = e*h + delta*x*B; returns the readout C.h + D x.
+    // State update h = e*h + delta2*x*B; returns the readout (C ln 2).h, i.e. C.h in natural
+    // units (the skip terms D x of both directions are added once, where the outputs meet). Two
+    // accumulation chains: the waves sharing a SIMD hide their latency, and one add joins them.
     template <bool kReadout>
     __device__ __forceinline__ float update(const Prelude& p, const float (&Cv)[kN]) {
-        float acc[4] = {p.dx, 0.0f, 0.0f, 0.0f};
+        float acc[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int n = 0; n < kN; ++n) {
             h[n] = fmaf(h[n], p.e[n], p.ub[n]);
-            if (kReadout) acc[n & 3] = fmaf(Cv[n], h[n], acc[n & 3]);
+            if (kReadout) acc[n & 1] = fmaf(Cv[n], h[n], acc[n & 1]);
         }
-        return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        return acc[0] + acc[1];
     }
 };
 
@@ -303,7 +313,6 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     constexpr bool kReadout = kMode != kAggregate;
     using E = typename IoTraits<IO>::elem;
     if (kbeg >= kend) return;
-    const bool fwd = c.dir == 0;
     const int len = c.t1 - c.t0;
     const int64_t row0 = static_cast<int64_t>(c.seq) * a.Lp + c.t0;  // first token row of the chunk
     const int64_t eoff = row0 * a.Di;
@@ -322,7 +331,12 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const uint32_t vo = static_cast<uint32_t>(c.dc) * e;
     const uint32_t vp = static_cast<uint32_t>(c.lane) * 4;
     const int last = kend - 1;
-    auto lt = [&](int k) { return fwd ? k : len - 1 - k; };  // local token index of walk step k
+    // Local token index of walk step k: k forward, len-1-k backward, as base + sign*k with
+    // wave-uniform base and sign. Both directions run this same code: a separate instance per
+    // direction puts two different hot loops on every CU and measured much slower.
+    const int sgn = 1 - 2 * c.dir;
+    const int tbase = c.dir * (len - 1);
+    auto lt = [&](int k) { return tbase + sgn * k; };
     auto toff = [&](int k) {  // token row byte offset of walk step min(k, last)
         return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lt(min(k, last)))) * rowb;
     };
@@ -345,7 +359,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     // step k. C rows come from the chunk's copy in LDS (staged once per workgroup), read as
     // wave-uniform broadcasts at the start of the step that uses them.
     float Bn[kN], Cv[kN];
-    ld_row(Bs + lt(kbeg) * kN, Bn);
+    ld_row(Bs, static_cast<uint32_t>(lt(kbeg)) * (kN * 4), Bn);
     auto lds_row = [&](int k, float (&v)[kN]) {
         const float4* cp = reinterpret_cast<const float4*>(lds_c + lt(min(k, last)) * kN);
 #pragma unroll
@@ -359,7 +373,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     };
     if (kReadout) lds_row(kbeg, Cv);
     Prelude cur = ln.template prelude<kDecay>(widen(IO{}, xr[0]), widen(IO{}, dr[0]), Bn);
-    ld_row(Bs + lt(min(kbeg + 1, last)) * kN, Bn);
+    ld_row(Bs, static_cast<uint32_t>(lt(min(kbeg + 1, last))) * (kN * 4), Bn);
     {
         const uint32_t so = toff(kbeg + P);
         xr[0] = ld_raw(IO{}, rx, vo, so);
@@ -393,8 +407,8 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
         // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
         const Prelude nxt = ln.template prelude<kDecay>(xn, dn, Bn);
-        ld_row(Bs + lt(min(kk + 2, last)) * kN, Bn);
-        if (kMode == kAggregate) dsum += cur.delta;
+        ld_row(Bs, static_cast<uint32_t>(lt(min(kk + 2, last))) * (kN * 4), Bn);
+        if (kMode == kAggregate) dsum += cur.delta2;
         const float yv = ln.template update<kReadout>(cur, Cv);
         if (kMode == kPark) {
             if (kGlobalPark)
@@ -410,7 +424,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             // transition form), and stores the same bits to the same element. Without the branch
             // the readout stays in the token's single basic block, where it interleaves with the
             // next token's prelude.
-            st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (yv + other));
+            st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * fmaf(ln.Dsum, cur.x, yv + other));
         }
         cur = nxt;
         if (kReadout) {
@@ -433,6 +447,15 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         if (k + j < kend) body(k + j, j);
 }
 
+// The walk instance for this wave's transition form (wave-uniform).
+template <typename IO, int kMode, bool kGlobalPark>
+__device__ __forceinline__ void walk_as(int form, const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
+                                        const float* lds_c, int kbeg, int kend, float& dsum) {
+    if (form == kGeometric) walk<IO, kGeometric, kMode, kGlobalPark>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+    else if (form == kProgression) walk<IO, kProgression, kMode, kGlobalPark>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+    else walk<IO, kGeneral, kMode, kGlobalPark>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+}
+
 // Widen the bf16 B rows to fp32 rows once per call: [B_f, B_b][tokens][16], read through the
 // scalar unit by the scan. One thread per 32-bit word (two bf16 values).
 __global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
@@ -448,7 +471,8 @@ __global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
     reinterpret_cast<float2*>(a.rows + which * a.tokens * kN)[w] = f;
 }
 
-// Copy the chunk's C rows of both directions into LDS as fp32: lds_c[dir][t][16], t in [0, len).
+// Copy the chunk's C rows of both directions into LDS as fp32 times ln 2 (the state is kept in
+// log2 units): lds_c[dir][t][16], t in [0, len).
 // Each direction's rows are one contiguous range of 32-bit words in memory; every thread issues
 // all its loads before widening and storing, so the copy costs one memory round trip.
 template <typename IO>
@@ -477,10 +501,10 @@ __device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& 
                 const int dir = i >= wpd ? 1 : 0;
                 float* dst = lds_c + dir * a.T * kN + (i - dir * wpd) * kPerWord;
                 if (kPerWord == 1) {
-                    dst[0] = __uint_as_float(w[u]);
+                    dst[0] = __uint_as_float(w[u]) * kLn2;
                 } else {
-                    dst[0] = __uint_as_float(w[u] << 16);
-                    dst[1] = __uint_as_float(w[u] & 0xffff0000u);
+                    dst[0] = __uint_as_float(w[u] << 16) * kLn2;
+                    dst[1] = __uint_as_float(w[u] & 0xffff0000u) * kLn2;
                 }
             }
         }
@@ -513,13 +537,9 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
     float unused = 0.0f;
     __syncthreads();  // the C rows are staged
-    if (form == kGeometric) walk<IO, kGeometric, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
-    else if (form == kProgression) walk<IO, kProgression, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
-    else walk<IO, kGeneral, kPark, kGlobalPark>(a, c, ln, lds_park, lds_c, 0, n1, unused);
+    walk_as<IO, kPark, kGlobalPark>(form, a, c, ln, lds_park, lds_c, 0, n1, unused);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
-    if (form == kGeometric) walk<IO, kGeometric, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
-    else if (form == kProgression) walk<IO, kProgression, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
-    else walk<IO, kGeneral, kFinish, kGlobalPark>(a, c, ln, lds_park, lds_c, n1, len, unused);
+    walk_as<IO, kFinish, kGlobalPark>(form, a, c, ln, lds_park, lds_c, n1, len, unused);
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
@@ -534,9 +554,7 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     const int form = ln.decay_form(a, c.dir, c.dc);
     const int len = c.t1 - c.t0;
     float s = 0.0f;
-    if (form == kGeometric) walk<IO, kGeometric, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, len, s);
-    else if (form == kProgression) walk<IO, kProgression, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, len, s);
-    else walk<IO, kGeneral, kAggregate, false>(a, c, ln, nullptr, nullptr, 0, len, s);
+    walk_as<IO, kAggregate, false>(form, a, c, ln, nullptr, nullptr, 0, len, s);
     if (c.valid) {
         const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
         float* dst = a.carry + slot * kN * a.Di;
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
     const int dir = static_cast<int>(blockIdx.z) & 1;
     const int seq = static_cast<int>(blockIdx.z) >> 1;
     if (d >= a.Di) return;
-    const float a2 = a.A[dir][d * kN + n] * kLog2e;
+    const float an = a.A[dir][d * kN + n];
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
     float H = 0.0f;
     for (int k = 0; k < a.K; ++k) {
@@ -567,7 +585,7 @@ __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
         const float s = a.dsum[slot * a.Di + d];
         const float end = *e;
         *e = H;
-        H = fmaf(fast_exp2(a2 * s), H, end);
+        H = fmaf(fast_exp2(an * s), H, end);
     }
 }
 
@@ -685,7 +703,7 @@ void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
 }
 
 template <typename IO>
-int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s) {
+int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (p.widen) {
         const int64_t threads = a.tokens * (kN / 2) * 2;
         hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
@@ -696,9 +714,13 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s) {
         const dim3 cgrid(static_cast<unsigned>(p.ncb), 4, static_cast<unsigned>(2 * p.nseq));
         hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
+    const bool timed = ev0 != nullptr && ev1 != nullptr;
+    if (timed && hipEventRecord(ev0, s) != hipSuccess) return VIMSCAN_ERR_HIP;
     if (p.park_global) launch_scan<IO, true>(a, p, s, p.K > 1);
     else launch_scan<IO, false>(a, p, s, p.K > 1);
-    return hipGetLastError() == hipSuccess ? VIMSCAN_OK : VIMSCAN_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return VIMSCAN_ERR_HIP;
+    if (timed && hipEventRecord(ev1, s) != hipSuccess) return VIMSCAN_ERR_HIP;
+    return VIMSCAN_OK;
 }
 
 }  // namespace
@@ -736,7 +758,7 @@ const char* vimscan_status_string(int status) {
     return kStatusText[i];
 }
 
-const char* vimscan_version(void) { return "vimscan 0.2.0 gfx950"; }
+const char* vimscan_version(void) { return "vimscan 0.3.0 gfx950"; }
 
 int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* B_f, const void* C_f,
                       const void* B_b, const void* C_b, const float* A_f, const float* A_b, const float* D_f,
@@ -814,7 +836,9 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
     a.subs = static_cast<int>(p.subs);
     a.general = (launch->flags & VIMSCAN_FLAG_GENERAL_DECAY) ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(launch->stream);
-    rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float>(a, p, s) : launch_all<Bf16>(a, p, s);
+    hipEvent_t ev0 = static_cast<hipEvent_t>(launch->scan_events[0]);
+    hipEvent_t ev1 = static_cast<hipEvent_t>(launch->scan_events[1]);
+    rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float>(a, p, s, ev0, ev1) : launch_all<Bf16>(a, p, s, ev0, ev1);
     return rc;
 }
 

@@ -88,6 +88,11 @@ typedef struct vimscan_launch {
                                may be NULL when that size is 0 */
     size_t workspace_bytes; /* size of workspace */
     void* stream;           /* hipStream_t to queue the work on; NULL = the null stream */
+    void* scan_events[2];   /* optional pair of hipEvent_t created by the caller: when both are
+                               non-NULL, the call records scan_events[0] on the stream just
+                               before the main scan kernel and scan_events[1] just after it, so
+                               the caller can time that kernel alone; NULL: nothing recorded.
+                               A failed record returns VIMSCAN_ERR_HIP. */
 } vimscan_launch;
 
 /* How a call with this launch is executed (for reporting and tests). */
@@ -97,11 +102,15 @@ typedef struct vimscan_plan {
     int64_t chunk_len;      /* tokens per chunk */
     int64_t chunks;         /* chunks per sequence; 1 = single pass, no workspace */
     int64_t workgroups;     /* workgroups of the main scan kernel */
-    int32_t kernels;        /* kernels launched per call: 1 (single pass) or 3 (chunked) */
+    int32_t kernels;        /* kernels launched per call: the main scan, plus 2 when chunked
+                               (chunk aggregates, carry combine), plus 1 for bf16 io (the
+                               pre-pass that widens the B rows to fp32) */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */
-    size_t workspace_bytes; /* scratch this call needs: chunk carries when chunks > 1, plus
-                               chunk_len*64*4 bytes per workgroup when park_in_workspace */
+    size_t workspace_bytes; /* scratch this call needs: chunk carries and delta sums when
+                               chunks > 1, chunk_len*64*4 bytes per wave pair when
+                               park_in_workspace, and the widened fp32 B rows
+                               (2*batch*seqlen*16*4 bytes) for bf16 io */
 } vimscan_plan;
 
 /*
@@ -122,14 +131,14 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
    ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */
 int vimscan_plan_launch(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan);
 
-/* Scratch bytes a call with this launch and seg_len needs (0 for a single pass over short
-   sequences). Host only. */
+/* Scratch bytes a call with this launch and seg_len needs (0 for an fp32 single pass whose
+   park fits in LDS). Host only. */
 int vimscan_workspace_bytes(const vimscan_launch* launch, int64_t seg_len, size_t* bytes);
 
 /* Static text for a status code; never NULL. */
 const char* vimscan_status_string(int status);
 
-/* Library version string, e.g. "vimscan 0.1.0 gfx950". */
+/* Library version string, e.g. "vimscan 0.3.0 gfx950". */
 const char* vimscan_version(void);
 
 #ifdef __cplusplus

@@ -8,6 +8,13 @@
       --workload <name> --source <kernel source file> --cmd "<commands>" --out profiles/<name>.json
       HBM traffic per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
       each scaled by what the same counter reads for a plain copy of N bytes.
+
+  python profile_summary.py valu --pmc <counter csv> --kernel <substring> --cus 256 --cmd "<command>"
+      --out profiles/<name>.txt
+      VALU issue evidence for one kernel from SQ counters (per dispatch, averaged): instructions per
+      wave, the fraction of time the VALU was busy (SQ_ACTIVE_INST_VALU is in quad-cycles per SIMD,
+      so busy = sum / CUs / GRBM_GUI_ACTIVE of one XCD), the shader clock implied by
+      GRBM_GUI_ACTIVE over the dispatch time, and the share of waves' time spent waiting.
 """
 from __future__ import annotations
 
@@ -60,7 +67,48 @@ def main():
     for k in ("fetch", "write", "calib_fetch", "calib_write", "kernel", "workload", "source", "cmd", "out"):
         f.add_argument("--" + k.replace("_", "-"), required=True)
     f.add_argument("--calib-bytes", type=int, required=True)
+    v = sub.add_parser("valu")
+    for k in ("pmc", "kernel", "cmd", "out"):
+        v.add_argument("--" + k, required=True)
+    v.add_argument("--cus", type=int, default=256)
+    v.add_argument("--xcds", type=int, default=8)
     a = ap.parse_args()
+
+    if a.what == "valu":
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        dur = {}
+        for r in csv.DictReader(open(a.pmc)):
+            if a.kernel in r["Kernel_Name"]:
+                per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+                dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if not per:
+            raise SystemExit(f"no dispatches of {a.kernel!r} in {a.pmc}")
+        names = sorted({k for d in per.values() for k in d})
+        mean = {k: statistics.mean(d[k] for d in per.values()) for k in names}
+        dns = statistics.mean(dur.values())
+        gui = mean["GRBM_GUI_ACTIVE"] / a.xcds            # cycles of one XCD (the counter sums the XCDs)
+        waves = mean["SQ_WAVES"]
+        lines = [f"command: {a.cmd}", f"kernel: {a.kernel} ({len(per)} dispatches, averaged)", "",
+                 "raw counters per dispatch:"]
+        lines += [f"  {k:28s} {mean[k]:16.0f}" for k in names]
+        lines += ["", "derived:",
+                  f"  dispatch time (profiled)      {dns / 1e3:10.2f} us",
+                  f"  shader clock                  {gui / dns:10.3f} GHz  (GRBM_GUI_ACTIVE per XCD / time)",
+                  f"  VALU instructions per wave    {mean['SQ_INSTS_VALU'] / waves:10.0f}"]
+        if "SQ_INSTS_VALU_TRANS_F32" in mean:
+            lines.append(f"  of them transcendental       {mean['SQ_INSTS_VALU_TRANS_F32'] / waves:10.0f}")
+        if "SQ_INSTS_SALU" in mean:
+            lines.append(f"  SALU instructions per wave    {mean['SQ_INSTS_SALU'] / waves:10.0f}")
+        lines += [f"  VALU busy                     {100 * mean['SQ_ACTIVE_INST_VALU'] / a.cus / gui:10.1f} %"
+                  "  (sum SQ_ACTIVE_INST_VALU / CUs / GRBM_GUI_ACTIVE per XCD)",
+                  f"  cycles per VALU instruction   {4 * mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_INSTS_VALU']:10.2f}"
+                  "  (per SIMD while busy)"]
+        if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+            lines.append(f"  waves waiting (any)           {100 * mean['SQ_WAIT_INST_ANY'] / mean['SQ_WAVE_CYCLES']:10.1f} %"
+                         "  of wave lifetime")
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
 
     if a.what == "trace":
         rows = kernel_stats(a.stats)

@@ -169,3 +169,23 @@ def test_workspace_bytes_rejects_bad_shapes(lib):
     assert lib.vimscan_workspace_bytes(ctypes.byref(_launch(d_state=4)), 0, ctypes.byref(need)) == SHAPE
     assert lib.vimscan_workspace_bytes(ctypes.byref(_launch()), 0, None) == NULL
     assert lib.vimscan_workspace_bytes(None, 0, ctypes.byref(need)) == NULL
+
+
+def _c_layout(struct, fields, tmp_path):
+    """sizeof and offsetof of a header struct, from a C program compiled against the header."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    body = "".join(f'    printf("%zu\\n", offsetof({struct}, {f}));\n' for f in fields)
+    src.write_text(f'#include <stddef.h>\n#include <stdio.h>\n#include "vimscan.h"\nint main(void) {{\n'
+                   f'    printf("%zu\\n", sizeof({struct}));\n{body}    return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    return [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+
+
+@pytest.mark.parametrize("cstruct,pystruct", [("vimscan_launch", binding._Launch), ("vimscan_plan", binding._Plan)])
+def test_binding_structs_match_the_header(cstruct, pystruct, tmp_path):
+    fields = [f for f, _ in pystruct._fields_]
+    size, *offsets = _c_layout(cstruct, fields, tmp_path)
+    assert size == ctypes.sizeof(pystruct)
+    assert offsets == [getattr(pystruct, f).offset for f in fields]

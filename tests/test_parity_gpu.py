@@ -11,7 +11,7 @@ from bidirectional_selective_scan_amd import binding
 from bidirectional_selective_scan_amd.configs import WORKLOADS
 from bidirectional_selective_scan_amd.inputs import (make_inputs, make_workload_inputs, progression_params,
                                                      random_params)
-from gpu_helpers import assert_close, run_gpu, to_device, to_f64
+from gpu_helpers import IO_NAMES, PARAM_NAMES, assert_close, run_gpu, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -160,3 +160,25 @@ def test_errors_are_reported():
         bad = dict(dev)
         bad["B_f"] = dev["B_f"][:, :, :8].contiguous()   # N = 8
         run_gpu(bad)
+
+
+def test_scan_events_time_the_main_kernel():
+    """The optional event pair in the launch is recorded around the main scan kernel only: its
+    interval is positive and inside the interval of the whole call; the result is unchanged."""
+    inp = _case(8, 197, 256, "bf16", seed=4)
+    dev = to_device(inp, "bf16")
+    call = binding.PreparedCall(*[dev[k] for k in IO_NAMES + PARAM_NAMES], seg_len=0)
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record(s)
+    torch.cuda.synchronize()
+    call.set_scan_events(ev[1].cuda_event, ev[2].cuda_event)
+    ev[0].record(s)
+    y = call()
+    ev[3].record(s)
+    torch.cuda.synchronize()
+    whole, scan = ev[0].elapsed_time(ev[3]), ev[1].elapsed_time(ev[2])
+    assert 0.0 < scan <= whole
+    assert ev[0].elapsed_time(ev[1]) >= 0.0 and ev[2].elapsed_time(ev[3]) >= 0.0
+    assert_close(to_f64(y), oracle.bidir_fwd(inp), "bf16", "timed call")
