@@ -115,3 +115,16 @@ def progression_params(d_inner: int, d_state: int, seed: int) -> dict:
         out["D_" + sfx] = rng.uniform(0.5, 1.5, size=d_inner).astype(np.float32)
         out["dt_bias_" + sfx] = rng.uniform(-5.0, 0.5, size=d_inner).astype(np.float32)
     return out
+
+
+def conv_params(d_inner: int, k: int, seed: int) -> dict:
+    """Depthwise convolution weights and biases for both directions, drawn like PyTorch's
+    default conv1d initialisation for a depthwise layer (fan-in k): U(-1/sqrt(k), 1/sqrt(k)).
+    Keys conv_w_f, conv_w_b (d_inner, k) and conv_b_f, conv_b_b (d_inner,), float32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bound = 1.0 / np.sqrt(k)
+    out = {}
+    for sfx in ("f", "b"):
+        out["conv_w_" + sfx] = rng.uniform(-bound, bound, size=(d_inner, k)).astype(np.float32)
+        out["conv_b_" + sfx] = rng.uniform(-bound, bound, size=d_inner).astype(np.float32)
+    return out

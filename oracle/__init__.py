@@ -14,7 +14,9 @@ Every part of the oracle is pinned by the ``not gpu`` tests against results fixe
 the SSD quadratic (matrix) form by brute force, the convolution form and the geometric-series
 closed form for a time-invariant system, the B = 0 skip path, the reversed-scan symmetry, the
 bidirectional-sum identity at A = 0, folding with a periodic reset, the worked one-step and
-decay examples, and a first-order IIR filter from scipy. No function here is parity unpinned.
+decay examples, and a first-order IIR filter from scipy. The directional convolution is pinned
+against torch's conv1d on zero-padded segments and the composed path against the plain scan run
+on the convolved inputs. No function here is parity unpinned.
 """
 from __future__ import annotations
 
@@ -56,6 +58,12 @@ def _declare(lib):
     lib.vimscan_oracle_silu.argtypes = [ctypes.c_double]
     lib.vimscan_oracle_max_threads.restype = ctypes.c_int
     lib.vimscan_oracle_max_threads.argtypes = []
+    lib.vimscan_oracle_dirconv_f64.restype = ctypes.c_int
+    lib.vimscan_oracle_dirconv_f64.argtypes = ([_D] * 3 + [ctypes.c_int64, ctypes.c_int] + [ctypes.c_int64] * 4
+                                               + [_D])
+    lib.vimscan_oracle_bidir_conv_f64.restype = ctypes.c_int
+    lib.vimscan_oracle_bidir_conv_f64.argtypes = ([_D] * 5 + [ctypes.c_int64] + [_D] * 12 + [ctypes.c_int64] * 5
+                                                  + [_D] * 3 + [ctypes.c_int])
     return lib
 
 
@@ -115,6 +123,53 @@ def bidir_fwd(inputs: dict, seg_len: int = 0, return_parts: bool = False, nthrea
     rc = lib.vimscan_oracle_bidir_f64(*[_ptr(a) for a in arrs], Bsz, L, Di, N, int(seg_len),
                                       _ptr(y), _ptr(yf) if yf is not None else null,
                                       _ptr(yb) if yb is not None else null, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return (y, yf, yb) if return_parts else y
+
+
+CONV_KEYS = ("conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b")
+
+
+def dirconv(x, w, cb, step: int, seg_len: int = 0, lib=None) -> np.ndarray:
+    """One direction's convolution + SiLU in float64: x (B, L, Di), w (Di, K), cb (Di,);
+    step +1 is the causal forward one, -1 the anti-causal backward one."""
+    lib = lib if lib is not None else _load()
+    x, w, cb = _f64(x), _f64(w), _f64(cb)
+    Bsz, L, Di = x.shape
+    if w.ndim != 2 or w.shape[0] != Di or cb.shape != (Di,):
+        raise ValueError("w must be (Di, K) and cb (Di,)")
+    u = np.empty_like(x)
+    rc = lib.vimscan_oracle_dirconv_f64(_ptr(x), _ptr(w), _ptr(cb), w.shape[1], int(step), Bsz, L, Di,
+                                        int(seg_len), _ptr(u))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return u
+
+
+def bidir_conv_fwd(inputs: dict, seg_len: int = 0, return_parts: bool = False, nthreads: int = 0, lib=None):
+    """The bidirectional scan with each direction's depthwise convolution + SiLU in front of it,
+    in float64. ``inputs`` holds the ``ARG_ORDER`` arrays plus conv_w_f, conv_w_b (Di, K) and
+    conv_b_f, conv_b_b (Di,). Returns y, or (y, y_fwd, y_bwd) with ``return_parts``."""
+    lib = lib if lib is not None else _load()
+    arrs = [_f64(inputs[k]) for k in ARG_ORDER]
+    cw_f, cb_f, cw_b, cb_b = (_f64(inputs[k]) for k in CONV_KEYS)
+    x = arrs[0]
+    if x.ndim != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner)")
+    Bsz, L, Di = x.shape
+    N = arrs[3].shape[-1]
+    K = cw_f.shape[-1]
+    if cw_f.shape != (Di, K) or cw_b.shape != (Di, K) or cb_f.shape != (Di,) or cb_b.shape != (Di,):
+        raise ValueError("conv weights must be (Di, K) and biases (Di,)")
+    y = np.empty((Bsz, L, Di), dtype=np.float64)
+    yf = np.empty_like(y) if return_parts else None
+    yb = np.empty_like(y) if return_parts else None
+    null = ctypes.cast(None, _D)
+    rc = lib.vimscan_oracle_bidir_conv_f64(_ptr(x), _ptr(cw_f), _ptr(cb_f), _ptr(cw_b), _ptr(cb_b), K,
+                                           *[_ptr(a) for a in arrs[1:]], Bsz, L, Di, N, int(seg_len),
+                                           _ptr(y), _ptr(yf) if yf is not None else null,
+                                           _ptr(yb) if yb is not None else null, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return (y, yf, yb) if return_parts else y

@@ -32,11 +32,25 @@
  *   scan enters, i.e. the state is set to 0 before the update: forward at t % seg_len == 0,
  *   backward at (t + 1) % seg_len == 0. seg_len == 0 means no reset.
  *
+ * Directional convolution in front of the scan (vimscan_oracle_bidir_conv_f64): each direction
+ * first passes x through its own depthwise 1D convolution followed by SiLU (Vim page, section
+ * 2.3: the forward and backward paths use 1D convolutions of opposite directions; SF-Mamba
+ * page, "MambaVision Mixer": SSM(SiLU(Conv(.)))), and that direction's scan then uses the result
+ * u in place of x, in delta * B * u and in the skip term D * u. The forward convolution is
+ * causal and the backward one anti-causal, each in its own walking order:
+ *     u_f[t] = silu(cb_f[d] + sum_{j=0}^{K-1} w_f[d][K-1-j] * x[t - j])
+ *     u_b[t] = silu(cb_b[d] + sum_{j=0}^{K-1} w_b[d][K-1-j] * x[t + j])
+ * (w[d][K-1] weights the current token, as a padded PyTorch conv1d weight [d][0][k] does.)
+ * Tokens outside the current segment count as zero (SF-Mamba page, "1D depthwise separable
+ * convolution adaptation": implicit padding at every segment boundary, so the convolution never
+ * crosses from one folded sequence into another).
+ *
  * Layouts (row-major, last index fastest):
  *   x, dt, z, y, yf, yb : [batch][seqlen][d_inner]
  *   B_f, C_f, B_b, C_b  : [batch][seqlen][d_state]
  *   A_f, A_b            : [d_inner][d_state]
  *   D_f, D_b, dt_bias_* : [d_inner]
+ *   conv w_f, w_b       : [d_inner][K];  conv cb_f, cb_b : [d_inner]
  */
 #include <math.h>
 #include <stdint.h>
@@ -56,7 +70,8 @@ double vimscan_oracle_softplus(double v) {
 double vimscan_oracle_silu(double v) { return v / (1.0 + exp(-v)); }
 
 /* One direction over one (b, d) channel. step = +1 (forward) or -1 (backward).
- * out[t] receives that direction's readout at the natural index t. */
+ * x is the direction's input (the shared x, or its convolved u). out[t] receives that
+ * direction's readout at the natural index t. */
 static void scan_one_direction(const double* x, const double* dt, const double* Bm, const double* Cm,
                                const double* A, double Dd, double dt_bias, int64_t b, int64_t d,
                                int64_t L, int64_t Di, int64_t N, int64_t seg_len, int step,
@@ -138,6 +153,100 @@ int vimscan_oracle_bidir_f64(const double* x, const double* dt, const double* z,
         free(of);
         free(ob);
     }
+    return err;
+}
+
+/* The directional convolution of one direction for every (b, t, d): u = silu(cb + taps . x),
+ * with taps walking back from t (step = +1, forward: x[t], x[t-1], ...) or forward from t
+ * (step = -1, backward: x[t], x[t+1], ...), zero outside t's segment. Returns 0 or -1. */
+int vimscan_oracle_dirconv_f64(const double* x, const double* w, const double* cb, int64_t k,
+                               int step, int64_t batch, int64_t seqlen, int64_t d_inner,
+                               int64_t seg_len, double* u) {
+    if (!x || !w || !cb || !u || k < 1 || (step != 1 && step != -1)) return -1;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || seg_len < 0) return -1;
+    if (seg_len > 0 && seqlen % seg_len != 0) return -1;
+    const int64_t L = seqlen, Di = d_inner, T = seg_len > 0 ? seg_len : seqlen;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t seg0 = (t / T) * T; /* first token of t's segment */
+            for (int64_t d = 0; d < Di; ++d) {
+                double acc = cb[d];
+                for (int64_t j = 0; j < k; ++j) {
+                    const int64_t s = t - step * j; /* the token j steps behind t in walk order */
+                    if (s < seg0 || s >= seg0 + T) continue;
+                    acc += w[d * k + (k - 1 - j)] * x[(b * L + s) * Di + d];
+                }
+                u[(b * L + t) * Di + d] = vimscan_oracle_silu(acc);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The bidirectional scan with the directional convolution in front of each direction (see the
+ * header): y = silu(z) * (scan_f(u_f) + scan_b(u_b)). Returns 0, -1 or -2 as above. */
+int vimscan_oracle_bidir_conv_f64(const double* x, const double* w_f, const double* cb_f,
+                                  const double* w_b, const double* cb_b, int64_t k,
+                                  const double* dt, const double* z, const double* B_f,
+                                  const double* C_f, const double* B_b, const double* C_b,
+                                  const double* A_f, const double* A_b, const double* D_f,
+                                  const double* D_b, const double* dt_bias_f,
+                                  const double* dt_bias_b, int64_t batch, int64_t seqlen,
+                                  int64_t d_inner, int64_t d_state, int64_t seg_len, double* y,
+                                  double* yf, double* yb, int nthreads) {
+    if (!x || !w_f || !cb_f || !w_b || !cb_b || !dt || !z || !B_f || !C_f || !B_b || !C_b ||
+        !A_f || !A_b || !D_f || !D_b || !dt_bias_f || !dt_bias_b || !y || k < 1)
+        return -1;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || seg_len < 0) return -1;
+    if (seg_len > 0 && seqlen % seg_len != 0) return -1;
+    const int64_t B = batch, L = seqlen, Di = d_inner, N = d_state;
+    if (B == 0 || L == 0 || Di == 0) return 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const size_t S = (size_t)(B * L * Di);
+    double* u_f = (double*)malloc(sizeof(double) * S);
+    double* u_b = (double*)malloc(sizeof(double) * S);
+    int err = (u_f && u_b) ? 0 : -2;
+    if (!err) err = vimscan_oracle_dirconv_f64(x, w_f, cb_f, k, +1, B, L, Di, seg_len, u_f);
+    if (!err) err = vimscan_oracle_dirconv_f64(x, w_b, cb_b, k, -1, B, L, Di, seg_len, u_b);
+    if (!err) {
+#pragma omp parallel
+        {
+            double* h = (double*)malloc(sizeof(double) * (size_t)N);
+            double* of = (double*)malloc(sizeof(double) * (size_t)L);
+            double* ob = (double*)malloc(sizeof(double) * (size_t)L);
+            const int ok = (h && of && ob);
+            if (!ok) {
+#pragma omp atomic write
+                err = -2;
+            }
+#pragma omp for collapse(2) schedule(static)
+            for (int64_t b = 0; b < B; ++b) {
+                for (int64_t d = 0; d < Di; ++d) {
+                    if (!ok) continue;
+                    scan_one_direction(u_f, dt, B_f, C_f, A_f, D_f[d], dt_bias_f[d], b, d, L, Di,
+                                       N, seg_len, +1, h, of);
+                    scan_one_direction(u_b, dt, B_b, C_b, A_b, D_b[d], dt_bias_b[d], b, d, L, Di,
+                                       N, seg_len, -1, h, ob);
+                    for (int64_t t = 0; t < L; ++t) {
+                        const int64_t i = (b * L + t) * Di + d;
+                        y[i] = vimscan_oracle_silu(z[i]) * (of[t] + ob[t]);
+                        if (yf) yf[i] = of[t];
+                        if (yb) yb[i] = ob[t];
+                    }
+                }
+            }
+            free(h);
+            free(of);
+            free(ob);
+        }
+    }
+    free(u_f);
+    free(u_b);
     return err;
 }
 
