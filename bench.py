@@ -111,6 +111,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=None, help="workload name (default: Vim-S)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-general", action="store_true", help="skip the forced general-decay measurement")
+    ap.add_argument("--no-conv", action="store_true",
+                    help="skip the measurement with the directional convolution (4 taps) in front of the scan")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte buffer 5 times (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -152,6 +154,11 @@ def main(argv=None):
 
     calls = {g: [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
                                       general_decay=g) for i in range(ncopy)] for g in (False, True)}
+    from bidirectional_selective_scan_amd.inputs import conv_params
+    cp = conv_params(w.d_inner, 4, w.seed + 101)
+    conv = tuple(torch.from_numpy(cp[k]).to(dev) for k in ("conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b"))
+    calls["conv"] = [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
+                                          conv=conv) for i in range(ncopy)]
 
     stream = torch.cuda.current_stream(dev)
 
@@ -163,8 +170,8 @@ def main(argv=None):
         torch.cuda.synchronize(dev)
         return evs
 
-    def timed(general):
-        cl = calls[general]
+    def timed(which):   # False: automatic transitions, True: forced general, "conv": with the convolution
+        cl = calls[which]
         for i in range(args.warmup):
             cl[i % ncopy]()
         torch.cuda.synchronize(dev)
@@ -239,6 +246,18 @@ def main(argv=None):
                                 "alu_achieved_tops": round(ops_g / kg / 1e12, 3),
                                 "alu_frac": round(ops_g / kg / 1e12 / VALU_PEAK_TOPS, 4),
                                 "ops_per_element": alu_ops_per_element(False)}
+    if not args.no_conv:
+        wall_c, per_call_c, per_scan_c = timed("conv")
+        kc = float(np.mean(per_scan_c))
+        cbytes = nbytes + 2 * w.d_inner * 5 * 4    # plus the taps and biases of both directions
+        # the convolution adds, per direction: 4 taps (FMAs), SiLU (3 ops + 2 transcendentals), and a
+        # second skip-term FMA instead of the shared one
+        ops_c = (alu_ops_per_element(geometric) + 2 * (4 + 3 + TRANS_OPS * 2) + 1) * w.tokens_channels
+        out["conv_fused"] = {"what": "directional depthwise conv1d (4 taps) + SiLU fused in front of both scans",
+                             "value": round(cbytes * args.steps / wall_c / 1e9, 2), "unit": "GB/s",
+                             "call_us": stats_us(per_call_c), "kernel_us": round(kc * 1e6, 3),
+                             "alu_achieved_tops": round(ops_c / kc / 1e12, 3),
+                             "alu_frac": round(ops_c / kc / 1e12 / VALU_PEAK_TOPS, 4)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out), flush=True)

@@ -41,8 +41,13 @@ class _Plan(ctypes.Structure):
                 ("park_in_workspace", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
 
-EXPORTED = ("vimscan_bidir_fwd", "vimscan_plan_launch", "vimscan_workspace_bytes", "vimscan_status_string",
-            "vimscan_version")
+class _Conv(ctypes.Structure):
+    _fields_ = [("w_f", ctypes.c_void_p), ("bias_f", ctypes.c_void_p), ("w_b", ctypes.c_void_p),
+                ("bias_b", ctypes.c_void_p), ("k", ctypes.c_int64)]
+
+
+EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_plan_launch", "vimscan_workspace_bytes",
+            "vimscan_status_string", "vimscan_version")
 
 
 def lib_path() -> str:
@@ -61,6 +66,9 @@ def load_library():
             vp = ctypes.c_void_p
             lib.vimscan_bidir_fwd.restype = ctypes.c_int
             lib.vimscan_bidir_fwd.argtypes = [vp] * 13 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
+            lib.vimscan_bidir_conv_fwd.restype = ctypes.c_int
+            lib.vimscan_bidir_conv_fwd.argtypes = ([vp, ctypes.POINTER(_Conv)] + [vp] * 12
+                                                   + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)])
             lib.vimscan_plan_launch.restype = ctypes.c_int
             lib.vimscan_plan_launch.argtypes = [ctypes.POINTER(_Launch), ctypes.c_int64, ctypes.POINTER(_Plan)]
             lib.vimscan_workspace_bytes.restype = ctypes.c_int
@@ -121,7 +129,8 @@ class PreparedCall:
     torch's current stream for x's device at preparation time unless ``stream`` is given."""
 
     def __init__(self, x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
-                 out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, stream=None):
+                 out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, stream=None,
+                 conv=None):
         lib = load_library()
         ios = (x, dt, z, B_f, C_f, B_b, C_b)
         params = (A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b)
@@ -142,6 +151,16 @@ class PreparedCall:
         for t, shp in zip(params, pshapes):
             if t.device != dev or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
                 raise ValueError("A_* (Di,N) and D_*, dt_bias_* (Di,) must be contiguous float32 on x's device")
+        cstruct = None
+        if conv is not None:
+            w_f, b_f, w_b, b_b = conv
+            K = w_f.shape[-1] if w_f.dim() == 2 else -1
+            for t, shp in zip((w_f, b_f, w_b, b_b), ((Di, K), (Di,), (Di, K), (Di,))):
+                if t.device != dev or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+                    raise ValueError("conv = (w_f, bias_f, w_b, bias_b): taps (Di,K) and biases (Di,), contiguous "
+                                     "float32 on x's device")
+            cstruct = _Conv(w_f.data_ptr(), b_f.data_ptr(), w_b.data_ptr(), b_b.data_ptr(), K)
+            params = params + tuple(conv)
         if out is None:
             out = torch.empty_like(x)
         elif out.device != dev or out.dtype != x.dtype or out.shape != x.shape or not out.is_contiguous():
@@ -159,8 +178,15 @@ class PreparedCall:
         self.out = out
         self._keep = (ios, params, out, workspace)   # keep every buffer alive while prepared
         self._launch = launch
-        self._fn = lib.vimscan_bidir_fwd
-        self._args = tuple(t.data_ptr() for t in ios + params) + (int(seg_len), out.data_ptr(), ctypes.byref(launch))
+        self._conv = cstruct
+        if cstruct is None:
+            self._fn = lib.vimscan_bidir_fwd
+            self._args = (tuple(t.data_ptr() for t in ios + params)
+                          + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
+        else:
+            self._fn = lib.vimscan_bidir_conv_fwd
+            self._args = ((x.data_ptr(), ctypes.byref(cstruct)) + tuple(t.data_ptr() for t in ios[1:] + params[:6])
+                          + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
 
     def set_scan_events(self, ev0: int = 0, ev1: int = 0):
         """hipEvent_t handles (e.g. torch.cuda.Event(...).cuda_event, already created) that the
@@ -174,12 +200,14 @@ class PreparedCall:
 
 
 def bidir_fwd(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
-              out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None):
+              out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, conv=None):
     """y = silu(z) * (forward selective scan + backward selective scan), on the GPU.
 
     x, dt, z: (B, L, Di); B_*, C_*: (B, L, 16), all float32 or all bfloat16, contiguous, on one
     CUDA(HIP) device. A_*: (Di, 16); D_*, dt_bias_*: (Di,), float32. seg_len: 0, or the period of
-    the state reset (must divide L). Returns y (B, L, Di) in x's dtype (``out`` if given).
+    the state reset (must divide L). conv: None, or (w_f, bias_f, w_b, bias_b) float32 taps (Di, K)
+    and biases (Di,) of the directional convolution + SiLU in front of each direction
+    (vimscan_bidir_conv_fwd). Returns y (B, L, Di) in x's dtype (``out`` if given).
     Queued on torch's current stream for x's device; does not synchronise."""
     return PreparedCall(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len, out,
-                        chunk_len, general_decay, workspace)()
+                        chunk_len, general_decay, workspace, conv=conv)()

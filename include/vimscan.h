@@ -62,7 +62,8 @@ enum vimscan_status {
     VIMSCAN_ERR_WORKSPACE = -7, /* workspace NULL or smaller than vimscan_workspace_bytes */
     VIMSCAN_ERR_HIP = -8,       /* a kernel launch failed (hipGetLastError after launching) */
     VIMSCAN_ERR_CHUNK = -9,     /* chunk_len < 0 */
-    VIMSCAN_ERR_FLAGS = -10     /* unknown bits in flags */
+    VIMSCAN_ERR_FLAGS = -10,    /* unknown bits in flags */
+    VIMSCAN_ERR_CONV = -11      /* vimscan_conv.k outside 1..4 */
 };
 
 /* dtype of x, dt, z, B_*, C_* and y. */
@@ -95,6 +96,28 @@ typedef struct vimscan_launch {
                                A failed record returns VIMSCAN_ERR_HIP. */
 } vimscan_launch;
 
+/*
+ * The directional depthwise convolution in front of the scan (vimscan_bidir_conv_fwd): each
+ * direction passes x through its own 1D depthwise convolution of k taps plus a bias, then SiLU,
+ * and scans the result u in place of x (in delta*B*u and in the skip term D*u). The forward
+ * convolution is causal and the backward one anti-causal, each in its own walking order
+ * (Vim page, section 2.3: the forward and backward paths use 1D convolutions of opposite
+ * directions; SF-Mamba page, "MambaVision Mixer": SSM(SiLU(Conv(.)))):
+ *   u_f[t] = silu(bias_f[d] + sum_{j=0}^{k-1} w_f[d][k-1-j] * x[t-j])
+ *   u_b[t] = silu(bias_b[d] + sum_{j=0}^{k-1} w_b[d][k-1-j] * x[t+j])
+ * so w[d][k-1] weights the current token, as in a PyTorch conv1d weight [d][0][k] with k-1
+ * zeros of padding on the side the direction comes from. Tokens outside the current sequence
+ * (the current segment when seg_len > 0) count as zero: the convolution never crosses a fold
+ * boundary (SF-Mamba page, "1D depthwise separable convolution adaptation").
+ */
+typedef struct vimscan_conv {
+    const float* w_f;       /* [d_inner][k] fp32 forward taps, device memory */
+    const float* bias_f;    /* [d_inner] fp32 */
+    const float* w_b;       /* [d_inner][k] fp32 backward taps */
+    const float* bias_b;    /* [d_inner] fp32 */
+    int64_t k;              /* taps, 1..4 (VIMSCAN_ERR_CONV otherwise) */
+} vimscan_conv;
+
 /* How a call with this launch is executed (for reporting and tests). */
 typedef struct vimscan_plan {
     int64_t sequences;      /* independent sequences: batch, or batch*seqlen/seg_len */
@@ -126,6 +149,20 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
                       const float* A_b, const float* D_f, const float* D_b,
                       const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
                       const vimscan_launch* launch);
+
+/*
+ * The same as vimscan_bidir_fwd with the directional convolution of *conv in front of each
+ * direction (see vimscan_conv). x is the convolution's input; conv and the arrays it points to
+ * are read only (host struct, device arrays 4-byte aligned) and must not overlap y or the
+ * workspace. Plan and workspace are those of vimscan_bidir_fwd for the same launch.
+ * Returns VIMSCAN_OK or a negative vimscan_status (VIMSCAN_ERR_NULL for a NULL conv or conv
+ * array, VIMSCAN_ERR_CONV for k outside 1..4, checked before the shape).
+ */
+int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* dt, const void* z,
+                           const void* B_f, const void* C_f, const void* B_b, const void* C_b,
+                           const float* A_f, const float* A_b, const float* D_f, const float* D_b,
+                           const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
+                           const vimscan_launch* launch);
 
 /* Fills *plan for a call with this launch and seg_len (workspace fields of launch are
    ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */

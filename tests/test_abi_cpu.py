@@ -14,7 +14,8 @@ from bidirectional_selective_scan_amd.configs import WORKLOADS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vimscan.h")
 
-OK, NULL, SHAPE, SEGLEN, DTYPE, ALIGN, ALIAS, WORKSPACE, HIP, CHUNK, FLAGS = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+OK, NULL, SHAPE, SEGLEN, DTYPE, ALIGN, ALIAS, WORKSPACE, HIP, CHUNK, FLAGS, CONV = (0, -1, -2, -3, -4, -5, -6, -7, -8,
+                                                                     -9, -10, -11)
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +41,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         s = binding.status_string(code)
         assert s and s != "unknown status"
     assert binding.status_string(-99) == "unknown status"
@@ -183,9 +184,48 @@ def _c_layout(struct, fields, tmp_path):
     return [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
 
 
-@pytest.mark.parametrize("cstruct,pystruct", [("vimscan_launch", binding._Launch), ("vimscan_plan", binding._Plan)])
+@pytest.mark.parametrize("cstruct,pystruct", [("vimscan_launch", binding._Launch), ("vimscan_plan", binding._Plan),
+                                               ("vimscan_conv", binding._Conv)])
 def test_binding_structs_match_the_header(cstruct, pystruct, tmp_path):
     fields = [f for f, _ in pystruct._fields_]
     size, *offsets = _c_layout(cstruct, fields, tmp_path)
     assert size == ctypes.sizeof(pystruct)
     assert offsets == [getattr(pystruct, f).offset for f in fields]
+
+
+def _conv(k=4, base=0x60000000):
+    return binding._Conv(base, base + 0x1000000, base + 0x2000000, base + 0x3000000, k)
+
+
+def _call_conv(lib, launch, conv, ptrs=None, seg_len=0, y=None):
+    p = ptrs or [0x10000000 * (i + 1) for i in range(13)]
+    y = 0x7F0000000 if y is None else y
+    return lib.vimscan_bidir_conv_fwd(p[0], ctypes.byref(conv) if conv is not None else None, *p[1:], seg_len, y,
+                                      ctypes.byref(launch) if launch is not None else None)
+
+
+def test_conv_arguments(lib):
+    assert _call_conv(lib, _launch(), None) == NULL
+    assert _call_conv(lib, None, _conv()) == NULL
+    for k in (0, 5, -1):
+        assert _call_conv(lib, _launch(d_state=3), _conv(k)) == CONV      # checked before the shape
+    assert _call_conv(lib, _launch(d_state=3), _conv(4)) == SHAPE
+    for f in ("w_f", "bias_f", "w_b", "bias_b"):
+        c = _conv()
+        setattr(c, f, 0)
+        assert _call_conv(lib, _launch(), c) == NULL
+        c = _conv()
+        setattr(c, f, getattr(c, f) + 2)
+        assert _call_conv(lib, _launch(), c) == ALIGN
+    # y (2*12*64 fp32) overlapping the backward taps (64*4 fp32)
+    c = _conv()
+    assert _call_conv(lib, _launch(), c, y=c.w_b - 4 * 2 * 12 * 64 + 4) == ALIAS
+    # the workspace overlapping a bias
+    launch = _launch(batch=1, seqlen=1025, d_inner=64)
+    need = ctypes.c_size_t(0)
+    assert lib.vimscan_workspace_bytes(ctypes.byref(launch), 0, ctypes.byref(need)) == OK
+    launch.workspace = c.bias_f - 64
+    launch.workspace_bytes = need.value
+    assert _call_conv(lib, launch, c) == ALIAS
+    # empty shapes still accept NULL arrays once conv itself is valid
+    assert _call_conv(lib, _launch(batch=0), _conv(), [0] * 13, y=0) == OK
