@@ -38,8 +38,10 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_vim_s.json")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_selective_scan_amd", "csrc", "vimscan.hip")
 
 # ALU work of the scan per (batch, token, channel), in fp32 VALU lane-operations: an FMA,
-# multiply, add, compare or select is one; a transcendental (exp2, log2, rcp) counts four, since
-# the VALU issues them at a quarter of the FMA rate. Per direction:
+# multiply, add, compare or select is one; a transcendental (exp2, log2, rcp) counts two: on the
+# scan kernel the SQ counters give 4.19 cycles per VALU instruction with 4.7% transcendental and
+# 4.76 with 19% (profiles/valu_*), i.e. 4 cycles per wave64 FMA and 8 per transcendental.
+# Per direction:
 #   softplus in log2 units: fma(dt, log2e, bias*log2e), exp2, +1, log2, compare, select
 #                                                                   4 ops + 2 transcendentals
 #   u = delta*x                                                     1 op
@@ -49,7 +51,7 @@ KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_selective_scan_amd", "csrc", "
 #   u*B[n]: 16 multiplies; state h = h*e + u*B: 16 FMAs; readout C.h: 16 FMAs + 1 add
 # Combine: yf + yb, + (D_f + D_b)*x, silu (-z*log2e, exp2, +1, rcp, *z), product
 #                                                                   6 ops + 2 transcendentals
-TRANS_OPS = 4
+TRANS_OPS = 2
 
 
 def alu_ops_per_element(geometric: bool) -> float:
@@ -231,7 +233,7 @@ def main(argv=None):
                      "kernel": "k_bidir_scan",
                      "ops_per_element": alu_ops_per_element(geometric),
                      "peak_basis": "fp32 VALU lane-operations per second without packed instructions "
-                                   "(256 CU x 64 lanes x 2.4 GHz); a transcendental counts 4",
+                                   "(256 CU x 64 lanes x 2.4 GHz); a transcendental counts 2",
                      # against the packed-instruction issue rate behind the published 157.3 TFLOP/s
                      "frac_of_packed_peak": round(alu_tops / (2 * VALU_PEAK_TOPS), 4),
                      "hbm": {"achieved": round(nbytes / kernel_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -1,7 +1,11 @@
 """Summaries of rocprofv3 output for profiles/.
 
   python profile_summary.py trace --stats <run_kernel_stats.csv> --cmd "<command>" --out profiles/<name>.txt
-      per-kernel call count and average / min / max duration from a --kernel-trace --stats run.
+      [--dispatches <run_kernel_trace.csv> --legs <kernel substring>=<label>:<n>,<label>:<n>,...]
+      per-kernel call count and average / min / max duration from a --kernel-trace --stats run;
+      with --legs, the dispatches of one kernel name are also split, in launch order, into
+      consecutive legs of the given sizes (e.g. a benchmark's automatic and forced-general runs
+      of the same kernel) and each leg is summarised.
 
   python profile_summary.py traffic --fetch <fetch counter csv> --write <write counter csv>
       --calib-fetch <csv> --calib-write <csv> --calib-bytes N --kernel <substring>
@@ -63,6 +67,9 @@ def main():
     t.add_argument("--stats", required=True)
     t.add_argument("--cmd", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--dispatches", default=None)
+    t.add_argument("--legs", default=None)
+    t.add_argument("--bench-json", default=None, help="the JSON line bench.py printed in the traced run")
     f = sub.add_parser("traffic")
     for k in ("fetch", "write", "calib_fetch", "calib_write", "kernel", "workload", "source", "cmd", "out"):
         f.add_argument("--" + k.replace("_", "-"), required=True)
@@ -71,6 +78,8 @@ def main():
     for k in ("pmc", "kernel", "cmd", "out"):
         v.add_argument("--" + k, required=True)
     v.add_argument("--cus", type=int, default=256)
+    v.add_argument("--skip", type=int, default=0, help="ignore the first N dispatches of the kernel")
+    v.add_argument("--take", type=int, default=0, help="then use N dispatches (0: all the rest)")
     v.add_argument("--xcds", type=int, default=8)
     a = ap.parse_args()
 
@@ -81,6 +90,11 @@ def main():
             if a.kernel in r["Kernel_Name"]:
                 per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
                 dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        order = sorted(per, key=int)[a.skip:]
+        if a.take:
+            order = order[:a.take]
+        per = {k: per[k] for k in order}
+        dur = {k: dur[k] for k in order}
         if not per:
             raise SystemExit(f"no dispatches of {a.kernel!r} in {a.pmc}")
         names = sorted({k for d in per.values() for k in d})
@@ -88,7 +102,8 @@ def main():
         dns = statistics.mean(dur.values())
         gui = mean["GRBM_GUI_ACTIVE"] / a.xcds            # cycles of one XCD (the counter sums the XCDs)
         waves = mean["SQ_WAVES"]
-        lines = [f"command: {a.cmd}", f"kernel: {a.kernel} ({len(per)} dispatches, averaged)", "",
+        lines = [f"command: {a.cmd}",
+                 f"kernel: {a.kernel} (dispatches {a.skip + 1}..{a.skip + len(per)} of the run, averaged)", "",
                  "raw counters per dispatch:"]
         lines += [f"  {k:28s} {mean[k]:16.0f}" for k in names]
         lines += ["", "derived:",
@@ -120,6 +135,31 @@ def main():
             lines.append(f"{short:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.3f} "
                          f"{float(r['MinNs']) / 1e3:10.3f} {float(r['MaxNs']) / 1e3:10.3f} "
                          f"{float(r['Percentage']):6.2f}%")
+        if a.dispatches and a.legs:
+            sub, spec = a.legs.split("=", 1)
+            durs = []
+            for r in csv.DictReader(open(a.dispatches)):
+                if sub in r["Kernel_Name"]:
+                    durs.append((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            durs = [d for _, d in sorted(durs)]
+            lines += ["", f"dispatches of the kernel whose name contains {sub!r}, in launch order:",
+                      f"{'leg':>12s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+            i = 0
+            for part in spec.split(","):
+                label, n = part.split(":")
+                leg = durs[i:i + int(n)]
+                i += int(n)
+                lines.append(f"{label:>12s} {len(leg):6d} {statistics.mean(leg) / 1e3:10.3f} "
+                             f"{statistics.median(leg) / 1e3:10.3f} {min(leg) / 1e3:10.3f} {max(leg) / 1e3:10.3f}")
+        if a.bench_json:
+            b = json.loads(open(a.bench_json).read().strip().splitlines()[-1])
+            lines += ["", "bench.py in the traced run (HIP events the library records around the scan kernel):",
+                      f"  automatic transitions   kernel_us mean {b['kernel_us']:.3f}, "
+                      f"median {b['scan_kernel_us']['median']:.3f}"]
+            if "general_decay" in b:
+                lines.append(f"  forced general          kernel_us mean {b['general_decay']['kernel_us']:.3f}")
+            if "conv_fused" in b:
+                lines.append(f"  with the convolution    kernel_us mean {b['conv_fused']['kernel_us']:.3f}")
         open(a.out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
