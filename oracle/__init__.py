@@ -64,6 +64,8 @@ def _declare(lib):
     lib.vimscan_oracle_bidir_conv_f64.restype = ctypes.c_int
     lib.vimscan_oracle_bidir_conv_f64.argtypes = ([_D] * 5 + [ctypes.c_int64] + [_D] * 12 + [ctypes.c_int64] * 5
                                                   + [_D] * 3 + [ctypes.c_int])
+    lib.vimscan_oracle_fwd_f64.restype = ctypes.c_int
+    lib.vimscan_oracle_fwd_f64.argtypes = [_D] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int, _D, ctypes.c_int]
     return lib
 
 
@@ -173,6 +175,33 @@ def bidir_conv_fwd(inputs: dict, seg_len: int = 0, return_parts: bool = False, n
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return (y, yf, yb) if return_parts else y
+
+
+FWD_ORDER = ("x", "dt", "z", "B", "C", "A", "D", "dt_bias")
+
+
+def fwd(inputs: dict, seg_len: int = 0, swap: bool = False, nthreads: int = 0, lib=None):
+    """The unidirectional (forward) scan, gated: y = silu(z) * (C.h + D x), in float64, with the
+    optional auxiliary swap of each sequence's (segment's) first and last output. ``inputs``
+    holds x, dt, z (B, L, Di), B, C (B, L, N), A (Di, N), D, dt_bias (Di,)."""
+    lib = lib if lib is not None else _load()
+    arrs = [_f64(inputs[k]) for k in FWD_ORDER]
+    x = arrs[0]
+    if x.ndim != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner)")
+    Bsz, L, Di = x.shape
+    N = arrs[3].shape[-1]
+    expect = {"x": (Bsz, L, Di), "dt": (Bsz, L, Di), "z": (Bsz, L, Di), "B": (Bsz, L, N), "C": (Bsz, L, N),
+              "A": (Di, N), "D": (Di,), "dt_bias": (Di,)}
+    for k, a in zip(FWD_ORDER, arrs):
+        if a.shape != expect[k]:
+            raise ValueError(f"{k}: shape {a.shape}, expected {expect[k]}")
+    y = np.empty((Bsz, L, Di), dtype=np.float64)
+    rc = lib.vimscan_oracle_fwd_f64(*[_ptr(a) for a in arrs], Bsz, L, Di, N, int(seg_len), int(bool(swap)), _ptr(y),
+                                    int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y
 
 
 def softplus(v: float) -> float:

@@ -45,6 +45,13 @@
  * convolution adaptation": implicit padding at every segment boundary, so the convolution never
  * crosses from one folded sequence into another).
  *
+ * Unidirectional scan with auxiliary-token swap (vimscan_oracle_fwd_f64; SF-Mamba page,
+ * "auxiliary patch swapping"): only the forward path, y_t = silu(z_t) * yf_t. The caller's
+ * sequence already holds the two auxiliary tokens at its first and last position; with swap != 0
+ * the outputs of the first and the last token of every sequence (every segment when
+ * seg_len > 0) are stored at each other's position, which is the page's exchange
+ * x_aux_head(i+1) = y_aux_tail(i), x_aux_tail(i+1) = y_aux_head(i) between layers.
+ *
  * Layouts (row-major, last index fastest):
  *   x, dt, z, y, yf, yb : [batch][seqlen][d_inner]
  *   B_f, C_f, B_b, C_b  : [batch][seqlen][d_state]
@@ -247,6 +254,54 @@ int vimscan_oracle_bidir_conv_f64(const double* x, const double* w_f, const doub
     }
     free(u_f);
     free(u_b);
+    return err;
+}
+
+/* Unidirectional (forward) scan, gate, and the optional auxiliary swap. Returns 0, -1 or -2. */
+int vimscan_oracle_fwd_f64(const double* x, const double* dt, const double* z, const double* Bm,
+                           const double* Cm, const double* A, const double* D, const double* dt_bias,
+                           int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                           int64_t seg_len, int swap, double* y, int nthreads) {
+    if (!x || !dt || !z || !Bm || !Cm || !A || !D || !dt_bias || !y) return -1;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || seg_len < 0) return -1;
+    if (seg_len > 0 && seqlen % seg_len != 0) return -1;
+    const int64_t B = batch, L = seqlen, Di = d_inner, N = d_state;
+    const int64_t T = seg_len > 0 ? seg_len : L;
+    if (B == 0 || L == 0 || Di == 0) return 0;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * (size_t)N);
+        double* of = (double*)malloc(sizeof(double) * (size_t)L);
+        const int ok = (h && of);
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for collapse(2) schedule(static)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t d = 0; d < Di; ++d) {
+                if (!ok) continue;
+                scan_one_direction(x, dt, Bm, Cm, A, D[d], dt_bias[d], b, d, L, Di, N, seg_len, +1,
+                                   h, of);
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t first = (t / T) * T, last = first + T - 1;
+                    int64_t dst = t;
+                    if (swap && t == first) dst = last;
+                    else if (swap && t == last) dst = first;
+                    const int64_t i = (b * L + t) * Di + d;
+                    y[(b * L + dst) * Di + d] = vimscan_oracle_silu(z[i]) * of[t];
+                }
+            }
+        }
+        free(h);
+        free(of);
+    }
     return err;
 }
 
