@@ -115,6 +115,8 @@ def main(argv=None):
     ap.add_argument("--no-general", action="store_true", help="skip the forced general-decay measurement")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip the measurement with the directional convolution (4 taps) in front of the scan")
+    ap.add_argument("--no-fwd", action="store_true",
+                    help="skip the forward-only scan measurements (with and without the auxiliary swap)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte buffer 5 times (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -161,6 +163,11 @@ def main(argv=None):
     conv = tuple(torch.from_numpy(cp[k]).to(dev) for k in ("conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b"))
     calls["conv"] = [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
                                           conv=conv) for i in range(ncopy)]
+    # forward only: x, dt, z, B_f, C_f and the forward parameters of the same inputs
+    for name, swap in (("fwd", False), ("fwd_swap", True)):
+        calls[name] = [binding.prepare_fwd(copies[i][0], copies[i][1], copies[i][2], copies[i][3], copies[i][4],
+                                           params[0], params[2], params[4], seg_len=w.seg_len, out=outs[i],
+                                           aux_swap=swap) for i in range(ncopy)]
 
     stream = torch.cuda.current_stream(dev)
 
@@ -260,6 +267,16 @@ def main(argv=None):
                              "call_us": stats_us(per_call_c), "kernel_us": round(kc * 1e6, 3),
                              "alu_achieved_tops": round(ops_c / kc / 1e12, 3),
                              "alu_frac": round(ops_c / kc / 1e12 / VALU_PEAK_TOPS, 4)}
+    if not args.no_fwd:
+        e_io = 2 if w.io_dtype == "bf16" else 4
+        fbytes = (w.tokens_channels * 4 * e_io + 2 * w.batch * w.seqlen * 16 * e_io
+                  + (w.d_inner * 16 + 2 * w.d_inner) * 4)
+        for name, label in (("fwd", "forward_only"), ("fwd_swap", "forward_only_aux_swap")):
+            wall_f, per_call_f, per_scan_f = timed(name)
+            out[label] = {"what": "forward scan alone (vimscan_fwd)" + (", with the auxiliary-token swap"
+                                                                         if name == "fwd_swap" else ""),
+                          "value": round(fbytes * args.steps / wall_f / 1e9, 2), "unit": "GB/s",
+                          "call_us": stats_us(per_call_f), "kernel_us": round(float(np.mean(per_scan_f)) * 1e6, 3)}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out), flush=True)

@@ -20,6 +20,8 @@ _lib = None
 VIMSCAN_F32 = 0
 VIMSCAN_BF16 = 1
 VIMSCAN_FLAG_GENERAL_DECAY = 1
+VIMSCAN_FLAG_AUX_SWAP = 2
+VIMSCAN_FLAG_FORWARD_ONLY = 4
 
 class VimscanError(RuntimeError):
     def __init__(self, status: int, text: str):
@@ -46,8 +48,8 @@ class _Conv(ctypes.Structure):
                 ("bias_b", ctypes.c_void_p), ("k", ctypes.c_int64)]
 
 
-EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_plan_launch", "vimscan_workspace_bytes",
-            "vimscan_status_string", "vimscan_version")
+EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_fwd", "vimscan_plan_launch",
+            "vimscan_workspace_bytes", "vimscan_status_string", "vimscan_version")
 
 
 def lib_path() -> str:
@@ -66,6 +68,8 @@ def load_library():
             vp = ctypes.c_void_p
             lib.vimscan_bidir_fwd.restype = ctypes.c_int
             lib.vimscan_bidir_fwd.argtypes = [vp] * 13 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
+            lib.vimscan_fwd.restype = ctypes.c_int
+            lib.vimscan_fwd.argtypes = [vp] * 8 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
             lib.vimscan_bidir_conv_fwd.restype = ctypes.c_int
             lib.vimscan_bidir_conv_fwd.argtypes = ([vp, ctypes.POINTER(_Conv)] + [vp] * 12
                                                    + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)])
@@ -100,24 +104,28 @@ def _io_code(dtype) -> int:
 
 
 def make_launch(batch, seqlen, d_inner, d_state=16, io_dtype=VIMSCAN_BF16, chunk_len=0, general_decay=False,
-                workspace=0, workspace_bytes=0, stream=0) -> _Launch:
-    return _Launch(int(batch), int(seqlen), int(d_inner), int(d_state), int(io_dtype),
-                   VIMSCAN_FLAG_GENERAL_DECAY if general_decay else 0, int(chunk_len), workspace or None,
-                   int(workspace_bytes), stream or None)
+                workspace=0, workspace_bytes=0, stream=0, aux_swap=False, forward_only=False) -> _Launch:
+    flags = ((VIMSCAN_FLAG_GENERAL_DECAY if general_decay else 0) | (VIMSCAN_FLAG_AUX_SWAP if aux_swap else 0)
+             | (VIMSCAN_FLAG_FORWARD_ONLY if forward_only else 0))
+    return _Launch(int(batch), int(seqlen), int(d_inner), int(d_state), int(io_dtype), flags, int(chunk_len),
+                   workspace or None, int(workspace_bytes), stream or None)
 
 
-def launch_info(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0) -> dict:
+def launch_info(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0, forward_only=False,
+                aux_swap=False) -> dict:
     """The library's execution plan for a call with this shape (host only)."""
     code = VIMSCAN_BF16 if io_dtype == "bf16" else VIMSCAN_F32
-    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len)
+    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len, aux_swap=aux_swap,
+                         forward_only=forward_only)
     plan = _Plan()
     _check(load_library().vimscan_plan_launch(ctypes.byref(launch), int(seg_len), ctypes.byref(plan)))
     return {f: getattr(plan, f) for f, _ in _Plan._fields_}
 
 
-def workspace_bytes(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0) -> int:
+def workspace_bytes(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0,
+                    forward_only=False) -> int:
     code = VIMSCAN_BF16 if io_dtype == "bf16" else VIMSCAN_F32
-    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len)
+    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len, forward_only=forward_only)
     n = ctypes.c_size_t(0)
     _check(load_library().vimscan_workspace_bytes(ctypes.byref(launch), int(seg_len), ctypes.byref(n)))
     return n.value
@@ -130,8 +138,10 @@ class PreparedCall:
 
     def __init__(self, x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
                  out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, stream=None,
-                 conv=None):
+                 conv=None, aux_swap: bool = False, forward_only: bool = False):
         lib = load_library()
+        if forward_only and conv is not None:
+            raise ValueError("the forward-only scan takes no convolution")
         ios = (x, dt, z, B_f, C_f, B_b, C_b)
         params = (A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b)
         if x.dim() != 3:
@@ -167,7 +177,8 @@ class PreparedCall:
             raise ValueError("out must match x")
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream
-        launch = make_launch(Bsz, L, Di, N, io, chunk_len, general_decay, 0, 0, stream)
+        launch = make_launch(Bsz, L, Di, N, io, chunk_len, general_decay, 0, 0, stream, aux_swap=aux_swap,
+                             forward_only=forward_only)
         need = ctypes.c_size_t(0)
         _check(lib.vimscan_workspace_bytes(ctypes.byref(launch), int(seg_len), ctypes.byref(need)))
         if need.value > 0:
@@ -179,7 +190,11 @@ class PreparedCall:
         self._keep = (ios, params, out, workspace)   # keep every buffer alive while prepared
         self._launch = launch
         self._conv = cstruct
-        if cstruct is None:
+        if forward_only:
+            self._fn = lib.vimscan_fwd
+            self._args = (tuple(t.data_ptr() for t in (x, dt, z, B_f, C_f, A_f, D_f, dt_bias_f))
+                          + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
+        elif cstruct is None:
             self._fn = lib.vimscan_bidir_fwd
             self._args = (tuple(t.data_ptr() for t in ios + params)
                           + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
@@ -200,7 +215,8 @@ class PreparedCall:
 
 
 def bidir_fwd(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
-              out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, conv=None):
+              out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, conv=None,
+              aux_swap: bool = False):
     """y = silu(z) * (forward selective scan + backward selective scan), on the GPU.
 
     x, dt, z: (B, L, Di); B_*, C_*: (B, L, 16), all float32 or all bfloat16, contiguous, on one
@@ -210,4 +226,19 @@ def bidir_fwd(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bi
     (vimscan_bidir_conv_fwd). Returns y (B, L, Di) in x's dtype (``out`` if given).
     Queued on torch's current stream for x's device; does not synchronise."""
     return PreparedCall(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len, out,
-                        chunk_len, general_decay, workspace, conv=conv)()
+                        chunk_len, general_decay, workspace, conv=conv, aux_swap=aux_swap)()
+
+
+def prepare_fwd(x, dt, z, B, C, A, D, dt_bias, seg_len: int = 0, out=None, chunk_len: int = 0,
+                general_decay: bool = False, aux_swap: bool = False, workspace=None, stream=None) -> PreparedCall:
+    """A prepared forward-only call (vimscan_fwd): x, dt, z (B, L, Di); B, C (B, L, 16); A (Di, 16);
+    D, dt_bias (Di,). ``aux_swap`` exchanges each sequence's first and last output after the scan."""
+    return PreparedCall(x, dt, z, B, C, B, C, A, A, D, D, dt_bias, dt_bias, seg_len, out, chunk_len, general_decay,
+                        workspace, stream, aux_swap=aux_swap, forward_only=True)
+
+
+def fwd(x, dt, z, B, C, A, D, dt_bias, seg_len: int = 0, out=None, chunk_len: int = 0, general_decay: bool = False,
+        aux_swap: bool = False, workspace=None):
+    """y = silu(z) * (C.h + D x) of the forward scan alone, on the GPU (vimscan_fwd); arguments as
+    ``prepare_fwd``. Queued on torch's current stream; does not synchronise."""
+    return prepare_fwd(x, dt, z, B, C, A, D, dt_bias, seg_len, out, chunk_len, general_decay, aux_swap, workspace)()

@@ -168,6 +168,7 @@ struct ScanArgs {
     const float* cw[2];  // directional convolution taps [Di][conv_k] (vimscan_bidir_conv_fwd)
     const float* cb[2];  // its biases [Di]
     int conv_k;          // taps, 1..kMaxTaps; 0 without the convolution
+    int uni;             // 1: forward only (vimscan_fwd): every wave of a workgroup is a channel block
 };
 
 // Taps of the directional convolution the kernels carry (a layer with fewer taps is run with
@@ -313,8 +314,8 @@ __device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a) {
     c.seq = rest / a.K;
     c.lane = static_cast<int>(threadIdx.x) & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    c.dir = wave & 1;
-    c.sub = wave >> 1;
+    c.dir = a.uni ? 0 : wave & 1;
+    c.sub = a.uni ? wave : wave >> 1;
     c.slot = lid * a.subs + c.sub;  // this wave pair's park region
     c.cb = cbw * a.subs + c.sub;    // may be past the last block when ncb is odd: y gets no stores
     c.d = c.cb * kWave + c.lane;
@@ -329,7 +330,8 @@ __device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a) {
 enum WalkMode {
     kPark = 0,      // first half of a chunk: park this direction's output (LDS or global scratch)
     kFinish = 1,    // second half: add the other direction's parked output, gate, store y
-    kAggregate = 2  // chunk pass 1: no readout, accumulate sum(delta)
+    kAggregate = 2, // chunk pass 1: no readout, accumulate sum(delta)
+    kOut = 3        // forward only: gate and store every token (no park, no other direction)
 };
 
 // x of one token by its raw bits (bf16 zero-extended), from the full tensor.
@@ -366,8 +368,8 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const __amdgpu_buffer_rsrc_t rx = chunk_rsrc(static_cast<const E*>(a.x) + eoff, span);
     const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(static_cast<const E*>(a.dt) + eoff, span);
     const __amdgpu_buffer_rsrc_t rz = chunk_rsrc(static_cast<const E*>(a.z) + eoff, span);
-    // A wave whose channel block lies past the last one (the spare half of the last workgroup
-    // when the number of blocks is odd) gets an empty y range: the hardware drops its stores.
+    // A wave whose channel block lies past the last one (the spare part of the last workgroup)
+    // gets an empty y range: the hardware drops its stores.
     const __amdgpu_buffer_rsrc_t ry = chunk_rsrc(static_cast<E*>(a.y) + eoff, c.cb < a.ncb ? span : 0u);
     const __amdgpu_buffer_rsrc_t rp =
         chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.slot) * a.T * kWave : nullptr,
@@ -418,9 +420,10 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         const uint32_t so = toff(kbeg + j);
         xr[j] = ld_raw(IO{}, rx, vo, so);
         dr[j] = ld_raw(IO{}, rd, vo, so);
-        if (kMode == kFinish) {
+        if (kMode == kFinish || kMode == kOut) {
             zr[j] = ld_raw(IO{}, rz, vo, so);
-            pr[j] = kGlobalPark ? __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kbeg + j), 0) : 0u;
+            pr[j] = (kMode == kFinish && kGlobalPark) ? __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kbeg + j), 0)
+                                                      : 0u;
         }
     }
     // B rows (SGPRs) run one token ahead: B(k+1) is consumed by the prelude of token k+1 during
@@ -458,7 +461,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         // needs no register copies (a copy would wait for the load just issued).
         const float xn = widen(IO{}, xr[jn]), dn = widen(IO{}, dr[jn]);
         float zv = 0.0f, pv = 0.0f;
-        if (kMode == kFinish) {
+        if (kMode == kFinish || kMode == kOut) {
             zv = widen(IO{}, zr[j]);
             pv = __uint_as_float(pr[j]);
         }
@@ -468,10 +471,10 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             xr[jn] = ld_raw(IO{}, rx, vo, so);
             dr[jn] = ld_raw(IO{}, rd, vo, so);
         }
-        if (kMode == kFinish) {
+        if (kMode == kFinish || kMode == kOut) {
             const uint32_t so = toff(kk + P);
             zr[j] = ld_raw(IO{}, rz, vo, so);
-            if (kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
+            if (kMode == kFinish && kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
         // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
         const Prelude nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
@@ -496,6 +499,8 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             const float ysum = kConv ? yv + other : fmaf(ln.Dsum, cur.x, yv + other);
             st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * ysum);
         }
+        if (kMode == kOut)
+            st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (kConv ? yv : fmaf(ln.Dd, cur.x, yv)));
         cur = nxt;
         if (kReadout) {
 #pragma unroll
@@ -559,18 +564,19 @@ __device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& 
         static_cast<const typename IoTraits<IO>::elem*>(a.Cm[0]) + row0 * kN);
     const uint32_t* src1 = reinterpret_cast<const uint32_t*>(
         static_cast<const typename IoTraits<IO>::elem*>(a.Cm[1]) + row0 * kN);
+    const int nw = (a.uni ? 1 : 2) * wpd;                     // words to stage (forward only: one direction)
     const int nt = static_cast<int>(blockDim.x);
-    for (int base = static_cast<int>(threadIdx.x); base < 2 * wpd; base += kU * nt) {
+    for (int base = static_cast<int>(threadIdx.x); base < nw; base += kU * nt) {
         uint32_t w[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int i = base + u * nt;
-            w[u] = i < wpd ? src0[i] : (i < 2 * wpd ? src1[i - wpd] : 0u);
+            w[u] = i < wpd ? src0[i] : (i < nw ? src1[i - wpd] : 0u);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int i = base + u * nt;
-            if (i < 2 * wpd) {
+            if (i < nw) {
                 const int dir = i >= wpd ? 1 : 0;
                 float* dst = lds_c + dir * a.T * kN + (i - dir * wpd) * kPerWord;
                 if (kPerWord == 1) {
@@ -616,6 +622,29 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     walk_as<IO, kFinish, kGlobalPark, kConv>(form, a, c, ln, lds_park, lds_c, n1, len, unused);
 }
 
+// Forward-only scan (vimscan_fwd): one chunk of one sequence, every wave a channel block of 64,
+// all walking forward; each token is gated and stored at once (no park, no meeting point).
+template <typename IO, bool kCarry>
+__global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
+    extern __shared__ float lds[];  // the chunk's C rows [T][16]
+    const WgCoords c = wg_coords(a);
+    stage_c_rows<IO>(a, c, lds);
+    Lane ln;
+    ln.init(a, 0, c.dc);
+    if (kCarry) {
+        const float* src = a.carry + (static_cast<int64_t>(c.seq) * a.K + c.chunk) * kN * a.Di;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ln.h[n] = src[n * static_cast<int64_t>(a.Di) + c.dc];
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
+    }
+    const int form = ln.decay_form(a, 0, c.dc);
+    float unused = 0.0f;
+    __syncthreads();  // the C rows are staged
+    walk_as<IO, kOut, false, false>(form, a, c, ln, nullptr, lds, 0, c.t1 - c.t0, unused);
+}
+
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
 // from a zero state, and the sum of delta over the chunk.
 template <typename IO, bool kConv>
@@ -643,12 +672,13 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
 // scan order; carry[chunk] is replaced by the state entering that chunk. The fold is the
 // associative operator of the linear recurrence: (P1, e1) then (P2, e2) -> (P1 P2, P2 e1 + e2),
 // with P = exp(A * sum delta) the chunk's transition product.
-// Block: 256 threads = 64 channels x 4 states; grid (channel blocks, 4, 2 * nseq).
+// Block: 256 threads = 64 channels x 4 states; grid (channel blocks, 4, 2 * nseq), or nseq in z
+// forward only.
 __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
     const int d = static_cast<int>(blockIdx.x) * kWave + (static_cast<int>(threadIdx.x) & (kWave - 1));
     const int n = static_cast<int>(blockIdx.y) * 4 + (static_cast<int>(threadIdx.x) >> 6);
-    const int dir = static_cast<int>(blockIdx.z) & 1;
-    const int seq = static_cast<int>(blockIdx.z) >> 1;
+    const int dir = a.uni ? 0 : static_cast<int>(blockIdx.z) & 1;
+    const int seq = a.uni ? static_cast<int>(blockIdx.z) : static_cast<int>(blockIdx.z) >> 1;
     if (d >= a.Di) return;
     const float an = a.A[dir][d * kN + n];
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
@@ -664,13 +694,29 @@ __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
     }
 }
 
+// Auxiliary-token swap after the scan (VIMSCAN_FLAG_AUX_SWAP): exchange the first and the last
+// row of y in every sequence (segment). One thread per (sequence, channel); grid (channel groups
+// of 256, sequences).
+template <typename IO>
+__global__ __launch_bounds__(256) void k_aux_swap(ScanArgs a) {
+    using E = typename IoTraits<IO>::elem;
+    const int d = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+    if (d >= a.Di || a.Lp < 2) return;
+    E* y = static_cast<E*>(a.y);
+    const int64_t first = static_cast<int64_t>(blockIdx.y) * a.Lp * a.Di + d;
+    const int64_t last = first + static_cast<int64_t>(a.Lp - 1) * a.Di;
+    const E v0 = y[first];
+    y[first] = y[last];
+    y[last] = v0;
+}
+
 // ------------------------------------------------------------------------------------------
 // Host side
 
 struct Plan {
     int64_t nseq, Lp, T, K, ncb, subs, wgs;
     int kernels;
-    bool park_global, widen;
+    bool park_global, widen, uni, swap;
     size_t ws;                                 // total scratch bytes
     size_t off_dsum, off_park, off_rows;      // byte offsets of the regions after the carries
 };
@@ -678,6 +724,11 @@ struct Plan {
 // A park larger than this goes to global scratch: in LDS it would cap a CU at fewer than 8
 // workgroups, and the VALU needs several waves per SIMD to issue at full rate.
 constexpr int64_t kLdsParkMaxBytes = 20 * 1024;
+
+// Forward only: a single pass needs at least this many waves (channel blocks x sequences), and a
+// chunked plan aims at this many.
+constexpr int64_t kUniSinglePass = 1024;
+constexpr int64_t kUniTarget = 3072;
 
 const char* const kStatusText[] = {
     "ok",
@@ -709,7 +760,9 @@ int check_shape(const vimscan_launch* l, int64_t seg_len) {
     if (seg_len < 0) return VIMSCAN_ERR_SEGLEN;
     if (seg_len > 0 && l->seqlen % seg_len != 0) return VIMSCAN_ERR_SEGLEN;
     if (l->chunk_len < 0) return VIMSCAN_ERR_CHUNK;
-    if (l->flags & ~VIMSCAN_FLAG_GENERAL_DECAY) return VIMSCAN_ERR_FLAGS;
+    if (l->flags & ~(VIMSCAN_FLAG_GENERAL_DECAY | VIMSCAN_FLAG_AUX_SWAP | VIMSCAN_FLAG_FORWARD_ONLY))
+        return VIMSCAN_ERR_FLAGS;
+
     return VIMSCAN_OK;
 }
 
@@ -723,16 +776,20 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     p->Lp = seg_len > 0 ? seg_len : l->seqlen;
     p->nseq = seg_len > 0 ? l->batch * (l->seqlen / seg_len) : l->batch;
     p->ncb = (l->d_inner + kWave - 1) / kWave;
-    const int64_t lanes = p->nseq * p->ncb;  // wave pairs (forward + backward) of a single pass
+    p->uni = (l->flags & VIMSCAN_FLAG_FORWARD_ONLY) != 0;
+    p->swap = (l->flags & VIMSCAN_FLAG_AUX_SWAP) != 0;
+    // Units of parallel work of a single pass: wave pairs (forward + backward), or single waves
+    // forward only; a chunked plan aims at 1536 of them (3 waves per SIMD bidirectional).
+    const int64_t lanes = p->nseq * p->ncb;
+    const int64_t target = p->uni ? kUniTarget : 1536;
     int64_t T;
     if (l->chunk_len > 0) {
         T = l->chunk_len;
-    } else if ((p->Lp <= kMaxChunk && lanes >= 256) || p->Lp <= 32) {
+    } else if ((p->Lp <= kMaxChunk && lanes >= (p->uni ? kUniSinglePass : 256)) || p->Lp <= 32) {
         T = p->Lp;  // single pass: enough workgroups, or too short to be worth chunking
     } else {
-        // Chunk for parallelism (about 1536 wave pairs = 3 waves per SIMD), with at least 32
-        // tokens per chunk.
-        int64_t K = (1536 + lanes - 1) / lanes;
+        // Chunk for parallelism with at least 32 tokens per chunk.
+        int64_t K = (target + lanes - 1) / lanes;
         const int64_t kmin = (p->Lp + kMaxChunk - 1) / kMaxChunk;
         const int64_t kmax = (p->Lp + 31) / 32;
         if (K < kmin) K = kmin;
@@ -743,19 +800,22 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     if (T > kMaxChunk) T = kMaxChunk;
     p->T = T;
     p->K = (p->Lp + T - 1) / T;
-    // Four waves per workgroup (two channel blocks x two directions) when there are two channel
-    // blocks: the hardware spreads a 4-wave workgroup over the CU's four SIMDs, where 2-wave
-    // workgroups can leave some SIMDs with twice the waves of others.
-    p->subs = p->ncb >= 2 ? 2 : 1;
+    // Four waves per workgroup (two channel blocks x two directions, or four channel blocks
+    // forward only) when there are enough channel blocks: the hardware spreads a 4-wave
+    // workgroup over the CU's four SIMDs, where 2-wave workgroups can leave some SIMDs with twice
+    // the waves of others.
+    if (p->uni) p->subs = p->ncb >= 4 ? 4 : p->ncb;
+    else p->subs = p->ncb >= 2 ? 2 : 1;
     p->wgs = p->nseq * p->K * ((p->ncb + p->subs - 1) / p->subs);
     p->widen = l->io_dtype == VIMSCAN_BF16;
-    p->kernels = (p->K > 1 ? 3 : 1) + (p->widen ? 1 : 0);
-    p->park_global = p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
+    p->kernels = (p->K > 1 ? 3 : 1) + (p->widen ? 1 : 0) + (p->swap ? 1 : 0);
+    p->park_global = !p->uni && p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
     const size_t f = sizeof(float);
-    const size_t carry = p->K > 1 ? static_cast<size_t>(2 * p->nseq * p->K) * kN * l->d_inner * f : 0;
-    const size_t dsum = p->K > 1 ? static_cast<size_t>(2 * p->nseq * p->K) * l->d_inner * f : 0;
+    const size_t ndir = p->uni ? 1 : 2;
+    const size_t carry = p->K > 1 ? static_cast<size_t>(ndir * p->nseq * p->K) * kN * l->d_inner * f : 0;
+    const size_t dsum = p->K > 1 ? static_cast<size_t>(ndir * p->nseq * p->K) * l->d_inner * f : 0;
     const size_t park = p->park_global ? static_cast<size_t>(p->wgs) * p->subs * p->T * kWave * f : 0;
-    const size_t rows = p->widen ? static_cast<size_t>(2) * l->batch * l->seqlen * kN * f : 0;
+    const size_t rows = p->widen ? ndir * l->batch * l->seqlen * kN * f : 0;
     p->off_dsum = round_up(carry, 256);
     p->off_park = round_up(p->off_dsum + dsum, 256);
     p->off_rows = round_up(p->off_park + park, 256);
@@ -770,9 +830,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return na > 0 && nb > 0 && a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Threads per workgroup: two waves (forward, backward) per channel block, or one forward only.
+unsigned wg_threads(const Plan& p) { return static_cast<unsigned>((p.uni ? 64 : 128) * p.subs); }
+
 template <typename IO, bool kGlobalPark, bool kConv>
 void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
-    const dim3 grid(static_cast<unsigned>(p.wgs)), block(static_cast<unsigned>(128 * p.subs));
+    const dim3 grid(static_cast<unsigned>(p.wgs)), block(wg_threads(p));
     const size_t lds = (2 * p.T * kN + (kGlobalPark ? 0 : p.subs * p.T * kWave)) * sizeof(float);
     if (carry) hipLaunchKernelGGL((k_bidir_scan<IO, true, kGlobalPark, kConv>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark, kConv>), grid, block, lds, s, a);
@@ -781,21 +844,35 @@ void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
 template <typename IO, bool kConv>
 int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (p.widen) {
-        const int64_t threads = a.tokens * (kN / 2) * 2;
+        const int64_t threads = a.tokens * (kN / 2) * (p.uni ? 1 : 2);
         hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
     }
     if (p.K > 1) {
-        hipLaunchKernelGGL((k_chunk_aggregate<IO, kConv>), dim3(static_cast<unsigned>(p.wgs)),
-                           dim3(static_cast<unsigned>(128 * p.subs)), 0, s, a);
-        const dim3 cgrid(static_cast<unsigned>(p.ncb), 4, static_cast<unsigned>(2 * p.nseq));
+        hipLaunchKernelGGL((k_chunk_aggregate<IO, kConv>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), 0,
+                           s, a);
+        const dim3 cgrid(static_cast<unsigned>(p.ncb), 4, static_cast<unsigned>((p.uni ? 1 : 2) * p.nseq));
         hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
     const bool timed = ev0 != nullptr && ev1 != nullptr;
     if (timed && hipEventRecord(ev0, s) != hipSuccess) return VIMSCAN_ERR_HIP;
-    if (p.park_global) launch_scan<IO, true, kConv>(a, p, s, p.K > 1);
-    else launch_scan<IO, false, kConv>(a, p, s, p.K > 1);
+    if (p.uni) {
+        const size_t lds = static_cast<size_t>(p.T) * kN * sizeof(float);
+        if (p.K > 1) hipLaunchKernelGGL((k_fwd_scan<IO, true>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
+                                        lds, s, a);
+        else hipLaunchKernelGGL((k_fwd_scan<IO, false>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), lds,
+                                s, a);
+    } else if (p.park_global) {
+        launch_scan<IO, true, kConv>(a, p, s, p.K > 1);
+    } else {
+        launch_scan<IO, false, kConv>(a, p, s, p.K > 1);
+    }
     if (hipGetLastError() != hipSuccess) return VIMSCAN_ERR_HIP;
     if (timed && hipEventRecord(ev1, s) != hipSuccess) return VIMSCAN_ERR_HIP;
+    if (p.swap) {
+        const dim3 sgrid(static_cast<unsigned>((a.Di + 255) / 256), static_cast<unsigned>(p.nseq));
+        hipLaunchKernelGGL(k_aux_swap<IO>, sgrid, dim3(256), 0, s, a);
+        if (hipGetLastError() != hipSuccess) return VIMSCAN_ERR_HIP;
+    }
     return VIMSCAN_OK;
 }
 
@@ -895,6 +972,7 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.cb[0] = conv ? conv->bias_f : nullptr;
     a.cb[1] = conv ? conv->bias_b : nullptr;
     a.conv_k = conv ? static_cast<int>(conv->k) : 0;
+    a.uni = p.uni ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(launch->stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(launch->scan_events[0]);
     hipEvent_t ev1 = static_cast<hipEvent_t>(launch->scan_events[1]);
@@ -948,8 +1026,18 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
                       const void* B_b, const void* C_b, const float* A_f, const float* A_b, const float* D_f,
                       const float* D_b, const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
                       const vimscan_launch* launch) {
+    if (launch && (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY)) return VIMSCAN_ERR_FLAGS;
     return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, nullptr, seg_len, y,
                       launch);
+}
+
+int vimscan_fwd(const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
+                const float* D, const float* dt_bias, int64_t seg_len, void* y, const vimscan_launch* launch) {
+    if (!launch) return VIMSCAN_ERR_NULL;
+    vimscan_launch l = *launch;
+    l.flags |= VIMSCAN_FLAG_FORWARD_ONLY;
+    // the forward parameters fill both direction slots; the forward-only kernels read slot 0
+    return bidir_impl(x, dt, z, B, C, B, C, A, A, D, D, dt_bias, dt_bias, nullptr, seg_len, y, &l);
 }
 
 int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* dt, const void* z,
@@ -957,6 +1045,7 @@ int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* 
                            const float* A_b, const float* D_f, const float* D_b, const float* dt_bias_f,
                            const float* dt_bias_b, int64_t seg_len, void* y, const vimscan_launch* launch) {
     if (!launch || !conv) return VIMSCAN_ERR_NULL;
+    if (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY) return VIMSCAN_ERR_FLAGS;
     if (conv->k < 1 || conv->k > kMaxTaps) return VIMSCAN_ERR_CONV;
     return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, conv, seg_len, y,
                       launch);

@@ -74,6 +74,15 @@ enum vimscan_io_dtype { VIMSCAN_F32 = 0, VIMSCAN_BF16 = 1 };
    an arithmetic progression in n, for which the library otherwise forms the transitions as
    exp(delta*A[d,0]) * exp(delta*(A[d,1]-A[d,0]))^n. Both give the defined result. */
 #define VIMSCAN_FLAG_GENERAL_DECAY 1
+/* Auxiliary-token swap (SF-Mamba page, "auxiliary patch swapping"): after the scan, exchange
+   the outputs of the first and the last token of every sequence (every segment when
+   seg_len > 0), i.e. the page's exchange of the head and tail auxiliary tokens between layers
+   (one more small kernel on the stream). For every entry point. */
+#define VIMSCAN_FLAG_AUX_SWAP 2
+/* The launch describes a forward-only call (vimscan_fwd). vimscan_fwd implies it; the planning
+   functions need it to size the forward-only plan; vimscan_bidir_fwd and vimscan_bidir_conv_fwd
+   reject it (VIMSCAN_ERR_FLAGS). */
+#define VIMSCAN_FLAG_FORWARD_ONLY 4
 
 /* Shape and launch description, passed by pointer to every entry point. */
 typedef struct vimscan_launch {
@@ -127,13 +136,15 @@ typedef struct vimscan_plan {
     int64_t workgroups;     /* workgroups of the main scan kernel */
     int32_t kernels;        /* kernels launched per call: the main scan, plus 2 when chunked
                                (chunk aggregates, carry combine), plus 1 for bf16 io (the
-                               pre-pass that widens the B rows to fp32) */
+                               pre-pass that widens the B rows to fp32), plus 1 with
+                               VIMSCAN_FLAG_AUX_SWAP */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */
     size_t workspace_bytes; /* scratch this call needs: chunk carries and delta sums when
                                chunks > 1, chunk_len*64*4 bytes per wave pair when
                                park_in_workspace, and the widened fp32 B rows
-                               (2*batch*seqlen*16*4 bytes) for bf16 io */
+                               (2*batch*seqlen*16*4 bytes, half that forward only) for bf16
+                               io */
 } vimscan_plan;
 
 /*
@@ -163,6 +174,18 @@ int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* 
                            const float* A_f, const float* A_b, const float* D_f, const float* D_b,
                            const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
                            const vimscan_launch* launch);
+
+/*
+ * Unidirectional scan (SF-Mamba page: Vim with a one-way scan and auxiliary patch swap): only
+ * the forward path of the definition above, gated:
+ *   y[b,t,d] = silu(z[b,t,d]) * (C[b,t,:] . h_t + D[d] x[b,t,d])
+ * with h_t from (A, B, D, dt_bias) as the forward direction of vimscan_bidir_fwd, the same
+ * layouts, reset, dtypes and errors; usually combined with VIMSCAN_FLAG_AUX_SWAP. Plan and
+ * workspace are those of a launch with VIMSCAN_FLAG_FORWARD_ONLY (implied here).
+ */
+int vimscan_fwd(const void* x, const void* dt, const void* z, const void* B, const void* C,
+                const float* A, const float* D, const float* dt_bias, int64_t seg_len, void* y,
+                const vimscan_launch* launch);
 
 /* Fills *plan for a call with this launch and seg_len (workspace fields of launch are
    ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */

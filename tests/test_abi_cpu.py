@@ -229,3 +229,50 @@ def test_conv_arguments(lib):
     assert _call_conv(lib, launch, c) == ALIAS
     # empty shapes still accept NULL arrays once conv itself is valid
     assert _call_conv(lib, _launch(batch=0), _conv(), [0] * 13, y=0) == OK
+
+
+def test_forward_only_plans(lib):
+    f = binding.launch_info(128, 197, 768, 16, 0, "bf16", forward_only=True)
+    b = binding.launch_info(128, 197, 768, 16, 0, "bf16")
+    # one wave per channel block: 4 blocks per workgroup; no park; B rows of one direction
+    assert f["park_in_workspace"] == 0
+    ncb = 768 // 64
+    assert f["workgroups"] == 128 * f["chunks"] * (ncb // 4)
+    if f["chunks"] == 1:
+        assert f["workspace_bytes"] == 128 * 197 * 16 * 4
+    assert b["workspace_bytes"] > f["workspace_bytes"]
+    s = binding.launch_info(128, 197, 768, 16, 0, "bf16", forward_only=True, aux_swap=True)
+    assert s["kernels"] == f["kernels"] + 1
+    hi = binding.launch_info(8, 1025, 768, 16, 0, "bf16", forward_only=True)
+    assert hi["chunks"] > 1 and hi["kernels"] == 4
+    carry = 8 * hi["chunks"] * 16 * 768 * 4
+    dsum = 8 * hi["chunks"] * 768 * 4
+    assert hi["workspace_bytes"] == carry + dsum + 8 * 1025 * 16 * 4
+
+
+def _call_fwd(lib, launch, ptrs=None, seg_len=0, y=None):
+    p = ptrs or [0x10000000 * (i + 1) for i in range(8)]
+    y = 0x7F0000000 if y is None else y
+    return lib.vimscan_fwd(*p, seg_len, y, ctypes.byref(launch) if launch is not None else None)
+
+
+def test_forward_only_arguments(lib):
+    assert _call_fwd(lib, None) == NULL
+    assert _call_fwd(lib, _launch(d_state=8)) == SHAPE
+    assert _call_fwd(lib, _launch(seqlen=12), seg_len=5) == SEGLEN
+    for i in range(8):
+        p = [0x10000000 * (j + 1) for j in range(8)]
+        p[i] = 0
+        assert _call_fwd(lib, _launch(), p) == NULL
+    assert _call_fwd(lib, _launch(batch=0), [0] * 8, y=0) == OK
+    launch = _launch()
+    launch.flags = 8
+    assert _call_fwd(lib, launch) == FLAGS
+    # the bidirectional entry points reject a forward-only launch
+    launch = _launch()
+    launch.flags = binding.VIMSCAN_FLAG_FORWARD_ONLY
+    assert _call(lib, launch) == FLAGS
+    assert _call_conv(lib, launch, _conv()) == FLAGS
+    # y overlapping B (2*12*16 fp32)
+    p = [0x10000000 * (j + 1) for j in range(8)]
+    assert _call_fwd(lib, _launch(), p, y=p[3] + 64) == ALIAS
