@@ -185,38 +185,42 @@ struct Prelude {
 // How a wave forms its 16 transitions (see Lane::prelude).
 enum Decay { kGeneral = 0, kProgression = 1, kGeometric = 2 };
 
-// A lane's A row in the form a walk uses it, loaded when the walk starts: no form's values stay
-// live through a walk of another form (the register peak is then that of one form).
+// A lane's A row in the form a walk uses it. The general form's 16 values are loaded when its
+// walk starts, so they are not live through walks of the other forms (the register peak is then
+// that of one form); the progression's two values come from the row the form vote read when the
+// kernel started, so a walk of those forms starts without waiting for a load.
 template <int kDecay> struct Rates;
 template <> struct Rates<kGeneral> {
     float an[kN];  // A[d, n]
-    __device__ __forceinline__ void load(const float* A) {
+    __device__ __forceinline__ void load(const float* A, float, float) {
 #pragma unroll
         for (int n = 0; n < kN; ++n) an[n] = A[n];
     }
 };
 template <> struct Rates<kProgression> {
     float a0, da;  // A[d, 0], A[d, 1] - A[d, 0]
-    __device__ __forceinline__ void load(const float* A) {
-        a0 = A[0];
-        da = A[1] - A[0];
+    __device__ __forceinline__ void load(const float*, float a0_, float da_) {
+        a0 = a0_;
+        da = da_;
     }
 };
 template <> struct Rates<kGeometric> {
     float da;      // A[d, 1] - A[d, 0] (== A[d, 0])
-    __device__ __forceinline__ void load(const float* A) { da = A[1] - A[0]; }
+    __device__ __forceinline__ void load(const float*, float, float da_) { da = da_; }
 };
 
 // Per-lane recurrence state of one direction over one channel.
 struct Lane {
     float h[kN];    // state scaled by log2(e)
+    float a0, da;       // A[d, 0], A[d, 1] - A[d, 0] (set by decay_form)
     float Dsum, bias2;  // D_f[d] + D_b[d] (the skip terms of both directions); dt_bias[d] * log2(e)
     float Dd;           // this direction's D[d] (with the convolution each direction has its own input)
     float ctap[kMaxTaps], cbias;  // convolution: ctap[j] weights the token j steps back in walk order
 
-    __device__ __forceinline__ void init(const ScanArgs& a, int dir, int dc) {
+    // own_skip: the walk adds this direction's D[d] * u itself (the convolution, forward only).
+    __device__ __forceinline__ void init(const ScanArgs& a, int dir, int dc, bool own_skip) {
         Dsum = a.D[0][dc] + a.D[1][dc];
-        Dd = a.D[dir][dc];
+        Dd = own_skip ? a.D[dir][dc] : 0.0f;
         bias2 = a.dtb[dir][dc] * kLog2e;
     }
 
@@ -228,22 +232,29 @@ struct Lane {
         cbias = a.cb[dir][dc];
     }
 
-    // True when A[d, :] is exactly A0 + n*(A1 - A0) in fp32.
+    // True when A[d, :] is exactly A0 + n*(A1 - A0) in fp32. The row is read whole, before any
+    // comparison (one memory round trip, no chain of loads behind branches).
     __device__ __forceinline__ bool is_progression(const ScanArgs& a, int dir, int dc) const {
-        const float* A = a.A[dir] + dc * kN;
-        const float s = A[1] - A[0];
+        const float* A = a.A[dir] + dc * kN;  // 4-byte aligned only
+        float r[kN];
+#pragma unroll
+        for (int n = 0; n < kN; ++n) r[n] = A[n];
+        const float s = r[1] - r[0];
         bool ok = true;
 #pragma unroll
-        for (int n = 0; n < kN; ++n) ok = ok && (A[n] == A[0] + static_cast<float>(n) * s);
+        for (int n = 0; n < kN; ++n) ok &= (r[n] == r[0] + static_cast<float>(n) * s);
         return ok;
     }
 
     // The transition form this wave uses: one form for all 64 lanes (a wave-wide vote).
-    __device__ __forceinline__ int decay_form(const ScanArgs& a, int dir, int dc) const {
+    // Also keeps A[d, 0] and A[d, 1] - A[d, 0] for the progression forms.
+    __device__ __forceinline__ int decay_form(const ScanArgs& a, int dir, int dc) {
+        const float* A = a.A[dir] + dc * kN;
+        a0 = A[0];
+        da = A[1] - A[0];
         if (a.general) return kGeneral;
         if (!__all(is_progression(a, dir, dc))) return kGeneral;
-        const float* A = a.A[dir] + dc * kN;
-        return __all(A[0] == A[1] - A[0]) ? kGeometric : kProgression;
+        return __all(a0 == da) ? kGeometric : kProgression;
     }
 
     // Transition forms: kGeneral takes one exponential per state; kProgression uses
@@ -303,7 +314,7 @@ struct WgCoords {
     bool valid;
 };
 
-__device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a) {
+__device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a, bool uni) {
     WgCoords c;
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int ncbw = (a.ncb + a.subs - 1) / a.subs;  // channel-block groups per sequence
@@ -314,8 +325,8 @@ __device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a) {
     c.seq = rest / a.K;
     c.lane = static_cast<int>(threadIdx.x) & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    c.dir = a.uni ? 0 : wave & 1;
-    c.sub = a.uni ? wave : wave >> 1;
+    c.dir = uni ? 0 : wave & 1;
+    c.sub = uni ? wave : wave >> 1;
     c.slot = lid * a.subs + c.sub;  // this wave pair's park region
     c.cb = cbw * a.subs + c.sub;    // may be past the last block when ncb is odd: y gets no stores
     c.d = c.cb * kWave + c.lane;
@@ -392,7 +403,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     };
 
     Rates<kDecay> rates;
-    rates.load(a.A[c.dir] + c.dc * kN);
+    rates.load(a.A[c.dir] + c.dc * kN, ln.a0, ln.da);
     float xw[kMaxTaps - 1];  // raw x (widened) of walk steps k-1, k-2, k-3
     if (kConv) {
 #pragma unroll
@@ -549,12 +560,35 @@ __global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
     reinterpret_cast<float2*>(a.rows + which * a.tokens * kN)[w] = f;
 }
 
+// The same when both B tensors are 16-byte aligned: one thread per 16 bytes (8 values), so the
+// pass moves the same bytes with a quarter of the threads.
+__global__ __launch_bounds__(256) void k_widen_rows16(ScanArgs a) {
+    const int64_t quads = a.tokens * (kN / 8);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= (a.uni ? 1 : 2) * quads) return;
+    const int which = static_cast<int>(i / quads);  // 0 B_f, 1 B_b
+    const int64_t q = i - which * quads;
+    const uint4 u = static_cast<const uint4*>(a.Bm[which])[q];
+    float4 lo, hi;
+    lo.x = __uint_as_float(u.x << 16);
+    lo.y = __uint_as_float(u.x & 0xffff0000u);
+    lo.z = __uint_as_float(u.y << 16);
+    lo.w = __uint_as_float(u.y & 0xffff0000u);
+    hi.x = __uint_as_float(u.z << 16);
+    hi.y = __uint_as_float(u.z & 0xffff0000u);
+    hi.z = __uint_as_float(u.w << 16);
+    hi.w = __uint_as_float(u.w & 0xffff0000u);
+    float4* dst = reinterpret_cast<float4*>(a.rows + which * a.tokens * kN) + 2 * q;
+    dst[0] = lo;
+    dst[1] = hi;
+}
+
 // Copy the chunk's C rows of both directions into LDS as fp32 times ln 2 (the state is kept in
 // log2 units): lds_c[dir][t][16], t in [0, len).
 // Each direction's rows are one contiguous range of 32-bit words in memory; every thread issues
 // all its loads before widening and storing, so the copy costs one memory round trip.
 template <typename IO>
-__device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& c, float* lds_c) {
+__device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& c, float* lds_c, bool uni) {
     constexpr int kU = 16;                                     // words per thread per pass
     constexpr int kPerWord = 4 / IoTraits<IO>::bytes;          // values per 32-bit word
     const int len = c.t1 - c.t0;
@@ -564,7 +598,7 @@ __device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& 
         static_cast<const typename IoTraits<IO>::elem*>(a.Cm[0]) + row0 * kN);
     const uint32_t* src1 = reinterpret_cast<const uint32_t*>(
         static_cast<const typename IoTraits<IO>::elem*>(a.Cm[1]) + row0 * kN);
-    const int nw = (a.uni ? 1 : 2) * wpd;                     // words to stage (forward only: one direction)
+    const int nw = (uni ? 1 : 2) * wpd;                     // words to stage (forward only: one direction)
     const int nt = static_cast<int>(blockDim.x);
     for (int base = static_cast<int>(threadIdx.x); base < nw; base += kU * nt) {
         uint32_t w[kU];
@@ -596,12 +630,12 @@ __device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& 
 template <typename IO, bool kCarry, bool kGlobalPark, bool kConv>
 __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     extern __shared__ float lds[];  // C rows [2][T][16], then the park [subs][T][64] when in LDS
-    const WgCoords c = wg_coords(a);
+    const WgCoords c = wg_coords(a, false);
     float* lds_c = lds + c.dir * a.T * kN;
     float* lds_park = lds + 2 * a.T * kN + c.sub * a.T * kWave;
-    stage_c_rows<IO>(a, c, lds);
+    stage_c_rows<IO>(a, c, lds, false);
     Lane ln;
-    ln.init(a, c.dir, c.dc);
+    ln.init(a, c.dir, c.dc, kConv);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
     if (kCarry) {
         const float* src = a.carry + ((static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk) * kN * a.Di;
@@ -627,10 +661,10 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
 template <typename IO, bool kCarry>
 __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
     extern __shared__ float lds[];  // the chunk's C rows [T][16]
-    const WgCoords c = wg_coords(a);
-    stage_c_rows<IO>(a, c, lds);
+    const WgCoords c = wg_coords(a, true);
+    stage_c_rows<IO>(a, c, lds, true);
     Lane ln;
-    ln.init(a, 0, c.dc);
+    ln.init(a, 0, c.dc, true);
     if (kCarry) {
         const float* src = a.carry + (static_cast<int64_t>(c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
@@ -649,9 +683,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
 // from a zero state, and the sum of delta over the chunk.
 template <typename IO, bool kConv>
 __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
-    const WgCoords c = wg_coords(a);
+    const WgCoords c = wg_coords(a, a.uni != 0);
     Lane ln;
-    ln.init(a, c.dir, c.dc);
+    ln.init(a, c.dir, c.dc, false);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
 #pragma unroll
     for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
@@ -844,8 +878,13 @@ void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
 template <typename IO, bool kConv>
 int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (p.widen) {
-        const int64_t threads = a.tokens * (kN / 2) * (p.uni ? 1 : 2);
-        hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
+        if (aligned(a.Bm[0], 16) && aligned(a.Bm[1], 16)) {
+            const int64_t threads = a.tokens * (kN / 8) * (p.uni ? 1 : 2);
+            hipLaunchKernelGGL(k_widen_rows16, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
+        } else {
+            const int64_t threads = a.tokens * (kN / 2) * (p.uni ? 1 : 2);
+            hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
+        }
     }
     if (p.K > 1) {
         hipLaunchKernelGGL((k_chunk_aggregate<IO, kConv>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), 0,

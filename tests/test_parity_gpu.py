@@ -182,3 +182,21 @@ def test_scan_events_time_the_main_kernel():
     assert 0.0 < scan <= whole
     assert ev[0].elapsed_time(ev[1]) >= 0.0 and ev[2].elapsed_time(ev[3]) >= 0.0
     assert_close(to_f64(y), oracle.bidir_fwd(inp), "bf16", "timed call")
+
+
+def test_b_rows_not_16_byte_aligned():
+    """bf16 B tensors at 4-byte (not 16-byte) aligned addresses take the one-word-per-thread
+    widening pass; the result is the same as from aligned copies."""
+    inp = _case(3, 97, 128, "bf16", seed=8)
+    dev = to_device(inp, "bf16")
+    y0 = run_gpu(dev).clone()
+    for k in ("B_f", "B_b"):
+        t = dev[k]
+        buf = torch.empty(t.numel() + 2, dtype=t.dtype, device=t.device)
+        view = buf[2:].view(t.shape)      # 4 bytes past a 256-byte aligned allocation
+        view.copy_(t)
+        assert view.data_ptr() % 16 == 4
+        dev[k] = view
+    y1 = run_gpu(dev)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    assert_close(to_f64(y1), oracle.bidir_fwd(inp), "bf16", "unaligned B")
