@@ -128,3 +128,24 @@ def conv_params(d_inner: int, k: int, seed: int) -> dict:
         out["conv_w_" + sfx] = rng.uniform(-bound, bound, size=(d_inner, k)).astype(np.float32)
         out["conv_b_" + sfx] = rng.uniform(-bound, bound, size=d_inner).astype(np.float32)
     return out
+
+
+NCSSD_NAMES = ("x", "B", "C", "m")
+
+
+def ncssd_inputs(batch: int, seqlen: int, d_inner: int, d_state: int = 16, io_dtype: str = "f32",
+                 seed: int = 0) -> dict:
+    """Inputs of the NC-SSD global-state form. One ``Generator(PCG64(seed))``, draws in this
+    order, all float32: x ~ N(0, 1) (B, L, Di); B, C ~ N(0, 1) (B, L, N) each; u ~ U(ln 1e-3, 0)
+    (B, L) and m = exp(exp(u)), the token weights: m is the reciprocal of a per-token decay
+    exp(-v) with v log-uniform in [1e-3, 1], so m lies in (1, e]. x, B and C are rounded to
+    ``io_dtype``; m stays float32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"x": rng.standard_normal((batch, seqlen, d_inner), dtype=np.float32)}
+    for name in ("B", "C"):
+        out[name] = rng.standard_normal((batch, seqlen, d_state), dtype=np.float32)
+    u = rng.uniform(np.log(1e-3), 0.0, size=(batch, seqlen))
+    out["m"] = np.exp(np.exp(u)).astype(np.float32)
+    for name in ("x", "B", "C"):
+        out[name] = round_to_io(out[name], io_dtype)
+    return out

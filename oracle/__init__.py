@@ -16,7 +16,10 @@ closed form for a time-invariant system, the B = 0 skip path, the reversed-scan 
 bidirectional-sum identity at A = 0, folding with a periodic reset, the worked one-step and
 decay examples, and a first-order IIR filter from scipy. The directional convolution is pinned
 against torch's conv1d on zero-padded segments and the composed path against the plain scan run
-on the convolved inputs. No function here is parity unpinned.
+on the convolved inputs. The NC-SSD global-state form is pinned against the running sums of its
+simplified recurrence in both directions (the bidirectional-sum identity), against the pinned scan
+at A = 0, and by the invariance of its state under a joint reordering of the tokens. No function
+here is parity unpinned.
 """
 from __future__ import annotations
 
@@ -66,6 +69,8 @@ def _declare(lib):
                                                   + [_D] * 3 + [ctypes.c_int])
     lib.vimscan_oracle_fwd_f64.restype = ctypes.c_int
     lib.vimscan_oracle_fwd_f64.argtypes = [_D] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int, _D, ctypes.c_int]
+    lib.vimscan_oracle_ncssd_f64.restype = ctypes.c_int
+    lib.vimscan_oracle_ncssd_f64.argtypes = [_D] * 4 + [ctypes.c_int64] * 5 + [_D, _D, ctypes.c_int]
     return lib
 
 
@@ -202,6 +207,29 @@ def fwd(inputs: dict, seg_len: int = 0, swap: bool = False, nthreads: int = 0, l
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return y
+
+
+def ncssd(x, B, C, m, seg_len: int = 0, return_state: bool = False, nthreads: int = 0, lib=None):
+    """NC-SSD, the non-causal global-state form (VSSD page, sections 4.2.3 to 4.2.5), in float64:
+    per sequence (segment when seg_len > 0) H = B^T (X . m) and y = C H. x (Bsz, L, Di);
+    B, C (Bsz, L, N); m (Bsz, L), the weight 1/A_j of every token. Returns y, or (y, H) with
+    ``return_state``, H of shape (Bsz * L / T, N, Di)."""
+    lib = lib if lib is not None else _load()
+    x, B, C, m = _f64(x), _f64(B), _f64(C), _f64(m)
+    if x.ndim != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner)")
+    Bsz, L, Di = x.shape
+    N = B.shape[-1]
+    if B.shape != (Bsz, L, N) or C.shape != (Bsz, L, N) or m.shape != (Bsz, L):
+        raise ValueError("B, C must be (batch, seqlen, d_state) and m (batch, seqlen)")
+    T = seg_len if seg_len > 0 else L
+    y = np.empty((Bsz, L, Di), dtype=np.float64)
+    H = np.empty((Bsz * L // max(T, 1), N, Di), dtype=np.float64) if return_state else None
+    rc = lib.vimscan_oracle_ncssd_f64(_ptr(x), _ptr(B), _ptr(C), _ptr(m), Bsz, L, Di, N, int(seg_len), _ptr(y),
+                                      _ptr(H) if H is not None else ctypes.cast(None, _D), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return (y, H) if return_state else y
 
 
 def softplus(v: float) -> float:

@@ -52,6 +52,17 @@
  * seg_len > 0) are stored at each other's position, which is the page's exchange
  * x_aux_head(i+1) = y_aux_tail(i), x_aux_tail(i+1) = y_aux_head(i) between layers.
  *
+ * Non-causal global-state form, NC-SSD (vimscan_oracle_ncssd_f64; VSSD page, sections 4.2.3 to
+ * 4.2.5). Dividing the SSD recurrence by the token's scalar transition A_t and keeping only the
+ * relative weights gives h(t) = h(t-1) + (1/A_t) B_t x(t); summing it in both directions and
+ * dropping the token's own term leaves one hidden state shared by every token of the sequence,
+ *     H = sum_j m_j * B_j (x) x_j,     m_j = 1 / A_j,
+ * read out by every token with its own C: y_i = C_i . H. In matrix form, per sequence,
+ * Y = C (B^T (X . m)), where X . m scales token j's row of X by m_j. With seg_len > 0 every
+ * segment of the stream is its own sequence with its own H. Layouts: x, y [batch][seqlen][d_inner];
+ * B, C [batch][seqlen][d_state]; m [batch][seqlen]; H (optional output)
+ * [batch * seqlen / T][d_state][d_inner].
+ *
  * Layouts (row-major, last index fastest):
  *   x, dt, z, y, yf, yb : [batch][seqlen][d_inner]
  *   B_f, C_f, B_b, C_b  : [batch][seqlen][d_state]
@@ -301,6 +312,60 @@ int vimscan_oracle_fwd_f64(const double* x, const double* dt, const double* z, c
         }
         free(h);
         free(of);
+    }
+    return err;
+}
+
+/* NC-SSD: y = C (B^T (X . m)) per sequence (segment). Returns 0, -1 (bad arguments) or -2 (no
+   memory). H may be NULL. */
+int vimscan_oracle_ncssd_f64(const double* x, const double* Bm, const double* Cm, const double* m,
+                             int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                             int64_t seg_len, double* y, double* H, int nthreads) {
+    if (!x || !Bm || !Cm || !m || !y) return -1;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || seg_len < 0) return -1;
+    if (seg_len > 0 && seqlen % seg_len != 0) return -1;
+    const int64_t Di = d_inner, N = d_state;
+    const int64_t T = seg_len > 0 ? seg_len : seqlen;
+    if (batch == 0 || seqlen == 0 || Di == 0) return 0;
+    const int64_t S = batch * seqlen / T; /* sequences: token t of sequence s is stream row s*T+t */
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* xm = (double*)malloc(sizeof(double) * (size_t)T);
+        double* h = (double*)malloc(sizeof(double) * (size_t)N);
+        const int ok = (xm && h);
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for collapse(2) schedule(static)
+        for (int64_t s = 0; s < S; ++s) {
+            for (int64_t d = 0; d < Di; ++d) {
+                if (!ok) continue;
+                /* X . m: every token's input weighted by m_j */
+                for (int64_t j = 0; j < T; ++j) xm[j] = x[(s * T + j) * Di + d] * m[s * T + j];
+                /* H = B^T (X . m): the global state, one column (channel d) of it */
+                for (int64_t n = 0; n < N; ++n) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < T; ++j) acc += Bm[(s * T + j) * N + n] * xm[j];
+                    h[n] = acc;
+                    if (H) H[(s * N + n) * Di + d] = acc;
+                }
+                /* Y = C H: every token reads the same state out with its own C row */
+                for (int64_t i = 0; i < T; ++i) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) acc += Cm[(s * T + i) * N + n] * h[n];
+                    y[(s * T + i) * Di + d] = acc;
+                }
+            }
+        }
+        free(xm);
+        free(h);
     }
     return err;
 }

@@ -69,3 +69,15 @@ def test_progression_params_are_exact_progressions():
         geometric = A[:, 1] == 2 * A[:, 0]
         assert geometric[64:128].all() and geometric[192:].all()
         assert not geometric[:64].all()
+
+
+def test_ncssd_inputs_recipe():
+    from bidirectional_selective_scan_amd.inputs import ncssd_inputs
+    a = ncssd_inputs(3, 11, 32, 16, "bf16", 4)
+    b = ncssd_inputs(3, 11, 32, 16, "bf16", 4)
+    for k in ("x", "B", "C", "m"):
+        assert np.array_equal(a[k], b[k]) and a[k].dtype == np.float32
+    assert a["x"].shape == (3, 11, 32) and a["B"].shape == (3, 11, 16) and a["m"].shape == (3, 11)
+    for k in ("x", "B", "C"):
+        np.testing.assert_array_equal(round_to_io(a[k], "bf16"), a[k])
+    assert (a["m"] > 1.0).all() and (a["m"] <= np.float32(np.e)).all()

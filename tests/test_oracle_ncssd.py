@@ -1,0 +1,178 @@
+"""Pins of the oracle's NC-SSD global-state form (VSSD page, sections 4.2.3 to 4.2.5), and a check
+that they catch plausible mistakes in it.
+
+Expectations come from routes that share nothing with the oracle's matrix-product loops: the
+simplified recurrence h(t) = h(t-1) + (1/A_t) B_t x(t) of section 4.2.3 run as running sums in
+both directions, whose sum minus the token's own term is the global state (section 4.2.4); the
+pinned selective scan at A = 0 (transition 1) with the step size set to m; the invariance of the
+state under any reordering of the tokens that section 4.2.4 states; closed forms for one-hot B and
+a single token; and folding. CPU only."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from bidirectional_selective_scan_amd.inputs import ncssd_inputs
+
+SRC = open(os.path.join(os.path.dirname(oracle.__file__), "vimscan_oracle.c")).read()
+
+
+def case(B, L, Di, N, seed):
+    return {k: np.asarray(v, dtype=np.float64) for k, v in ncssd_inputs(B, L, Di, N, "f32", seed).items()}
+
+
+def running_sums(f, seg_len=0):
+    """Global state per token from the simplified recurrence run forward and backward with
+    Python loops: hf(i) = hf(i-1) + m_i B_i x_i^T, hb(i) = hb(i+1) + m_i B_i x_i^T, each
+    restarted at every segment; H(i) = hf(i) + hb(i) - m_i B_i x_i^T. Returns H per token,
+    shape (Bsz, L, N, Di)."""
+    x, Bm, m = f["x"], f["B"], f["m"]
+    Bsz, L, Di = x.shape
+    N = Bm.shape[-1]
+    T = seg_len or L
+    out = np.zeros((Bsz, L, N, Di))
+    for b in range(Bsz):
+        for s0 in range(0, L, T):
+            z = [m[b, t] * np.outer(Bm[b, t], x[b, t]) for t in range(s0, s0 + T)]
+            hf, hb = [None] * T, [None] * T
+            acc = np.zeros((N, Di))
+            for i in range(T):
+                acc = acc + z[i]
+                hf[i] = acc
+            acc = np.zeros((N, Di))
+            for i in reversed(range(T)):
+                acc = acc + z[i]
+                hb[i] = acc
+            for i in range(T):
+                out[b, s0 + i] = hf[i] + hb[i] - z[i]
+    return out
+
+
+def from_running_sums(f, seg_len=0):
+    Hi = running_sums(f, seg_len)
+    return np.einsum("bln,blnd->bld", f["C"], Hi), Hi
+
+
+@pytest.mark.parametrize("B,L,Di,N,seg", [(2, 7, 3, 5, 0), (1, 12, 2, 4, 4), (3, 1, 4, 16, 0), (1, 9, 5, 16, 3)])
+def test_state_is_the_sum_of_both_running_sums(B, L, Di, N, seg):
+    f = case(B, L, Di, N, 100 + L)
+    y, H = oracle.ncssd(f["x"], f["B"], f["C"], f["m"], seg_len=seg, return_state=True)
+    y_ref, Hi = from_running_sums(f, seg)
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-12)
+    T = seg or L
+    for t in range(L):  # the state every token sees is the one global state of its segment
+        s = (np.arange(B) * (L // T)) + t // T
+        np.testing.assert_allclose(H[s], Hi[:, t], rtol=1e-12, atol=1e-12)
+
+
+def test_matches_the_scan_at_zero_transition_exponent():
+    """At A = 0 every transition is exp(0) = 1, so the pinned selective scan's forward branch is
+    the running sum of delta_j B_j x_j and its backward branch the reverse running sum; with
+    delta_j = m_j (dt = inverse softplus of m, no bias), D = 0 and the same B and C in both
+    directions, yf + yb = C_i . (H + m_i B_i x_i)."""
+    f = case(2, 11, 4, 16, 7)
+    Bsz, L, Di = f["x"].shape
+    inv_sp = f["m"] + np.log(-np.expm1(-f["m"]))
+    scan = {"x": f["x"], "dt": np.repeat(inv_sp[:, :, None], Di, axis=2), "z": np.ones_like(f["x"]),
+            "B_f": f["B"], "C_f": f["C"], "B_b": f["B"], "C_b": f["C"],
+            "A_f": np.zeros((Di, 16)), "A_b": np.zeros((Di, 16)), "D_f": np.zeros(Di), "D_b": np.zeros(Di),
+            "dt_bias_f": np.zeros(Di), "dt_bias_b": np.zeros(Di)}
+    _, yf, yb = oracle.bidir_fwd(scan, return_parts=True)
+    own = np.einsum("bln,bln->bl", f["C"], f["B"])[:, :, None] * f["m"][:, :, None] * f["x"]
+    np.testing.assert_allclose(oracle.ncssd(f["x"], f["B"], f["C"], f["m"]), yf + yb - own, rtol=1e-11, atol=1e-11)
+
+
+def test_state_ignores_token_order():
+    """The global state does not depend on where a token sits in the sequence (section 4.2.4):
+    reordering x, B and m together leaves every output unchanged when C stays in place."""
+    f = case(2, 13, 3, 8, 8)
+    perm = np.random.default_rng(5).permutation(13)
+    y0, H0 = oracle.ncssd(f["x"], f["B"], f["C"], f["m"], return_state=True)
+    y1, H1 = oracle.ncssd(f["x"][:, perm], f["B"][:, perm], f["C"], f["m"][:, perm], return_state=True)
+    np.testing.assert_allclose(H1, H0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y1, y0, rtol=1e-12, atol=1e-12)
+
+
+def test_one_hot_b_closed_form():
+    """B_j = e_k and m_j = w for every token: H[n] = w [n == k] sum_j x_j, y_i = C_i[k] w sum_j x_j."""
+    f = case(1, 6, 3, 4, 9)
+    k, w = 2, 1.75
+    Bm = np.zeros_like(f["B"])
+    Bm[..., k] = 1.0
+    y = oracle.ncssd(f["x"], Bm, f["C"], np.full_like(f["m"], w))
+    expect = f["C"][0, :, k][:, None] * w * f["x"][0].sum(axis=0)[None, :]
+    np.testing.assert_allclose(y[0], expect, rtol=1e-13, atol=1e-13)
+
+
+def test_single_token():
+    f = case(3, 1, 5, 16, 10)
+    expect = (f["C"][:, 0] * f["B"][:, 0]).sum(-1)[:, None] * f["m"][:, 0][:, None] * f["x"][:, 0]
+    np.testing.assert_allclose(oracle.ncssd(f["x"], f["B"], f["C"], f["m"])[:, 0], expect, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("k,T", [(4, 5), (3, 1)])
+def test_folded_equals_unfolded(k, T):
+    f = case(k, T, 6, 16, 11)
+    y_unf = oracle.ncssd(f["x"], f["B"], f["C"], f["m"])
+    fold = {n: a.reshape((1, k * T) + a.shape[2:]) for n, a in f.items()}
+    y_fold = oracle.ncssd(fold["x"], fold["B"], fold["C"], fold["m"], seg_len=T)
+    np.testing.assert_array_equal(y_fold.reshape(y_unf.shape), y_unf)
+
+
+def test_rejects_bad_arguments():
+    f = case(1, 6, 2, 4, 12)
+    with pytest.raises(ValueError):
+        oracle.ncssd(f["x"], f["B"], f["C"], f["m"], seg_len=4)
+    with pytest.raises(ValueError):
+        oracle.ncssd(f["x"], f["B"], f["C"], f["m"][:, :5])
+
+
+NCSSD_MUTATIONS = {
+    "drops_m": ("xm[j] = x[(s * T + j) * Di + d] * m[s * T + j];", "xm[j] = x[(s * T + j) * Di + d];"),
+    "m_of_mirrored_token": ("xm[j] = x[(s * T + j) * Di + d] * m[s * T + j];",
+                            "xm[j] = x[(s * T + j) * Di + d] * m[s * T + (T - 1 - j)];"),
+    "x_of_mirrored_channel": ("xm[j] = x[(s * T + j) * Di + d] * m[s * T + j];",
+                              "xm[j] = x[(s * T + j) * Di + (Di - 1 - d)] * m[s * T + j];"),
+    "state_takes_C": ("acc += Bm[(s * T + j) * N + n] * xm[j];", "acc += Cm[(s * T + j) * N + n] * xm[j];"),
+    "readout_takes_B": ("acc += Cm[(s * T + i) * N + n] * h[n];", "acc += Bm[(s * T + i) * N + n] * h[n];"),
+    "state_from_first_token": ("for (int64_t j = 0; j < T; ++j) acc += Bm", "for (int64_t j = 0; j < 1; ++j) acc += Bm"),
+    "readout_drops_last_state": ("for (int64_t n = 0; n < N; ++n) acc += Cm", "for (int64_t n = 0; n < N - 1; ++n) acc += Cm"),
+    "segments_ignored": ("const int64_t T = seg_len > 0 ? seg_len : seqlen;\n    if (batch == 0 || seqlen == 0 || Di == 0) return 0;\n    const int64_t S",
+                         "const int64_t T = seqlen;\n    if (batch == 0 || seqlen == 0 || Di == 0) return 0;\n    const int64_t S"),
+}
+
+
+def _build_variant(tmp_path, name, src):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"lib{name}.so"
+    c.write_text(src)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(so), str(c), "-lm"],
+                   check=True)
+    return oracle.load_variant(str(so))
+
+
+def _battery(lib):
+    failed = []
+    for name, (B, L, Di, N, seg) in {"plain": (2, 7, 3, 5, 0), "segments": (1, 12, 2, 4, 4)}.items():
+        f = case(B, L, Di, N, 100 + L)
+        try:
+            ok = np.allclose(oracle.ncssd(f["x"], f["B"], f["C"], f["m"], seg_len=seg, lib=lib),
+                             from_running_sums(f, seg)[0], rtol=1e-10, atol=1e-12)
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_battery(tmp_path):
+    assert _battery(_build_variant(tmp_path, "orig", SRC)) == []
+
+
+@pytest.mark.parametrize("name", sorted(NCSSD_MUTATIONS))
+def test_each_mutation_is_caught(tmp_path, name):
+    old, new = NCSSD_MUTATIONS[name]
+    assert SRC.count(old) == 1, f"pattern for {name} must occur once in the oracle source"
+    assert _battery(_build_variant(tmp_path, name, SRC.replace(old, new))), f"no pin caught {name}"
