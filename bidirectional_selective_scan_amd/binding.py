@@ -49,7 +49,8 @@ class _Conv(ctypes.Structure):
 
 
 EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_fwd", "vimscan_plan_launch",
-            "vimscan_workspace_bytes", "vimscan_status_string", "vimscan_version")
+            "vimscan_workspace_bytes", "vimscan_status_string", "vimscan_version", "vimscan_ncssd_fwd",
+            "vimscan_ncssd_plan")
 
 
 def lib_path() -> str:
@@ -82,6 +83,10 @@ def load_library():
             lib.vimscan_status_string.argtypes = [ctypes.c_int]
             lib.vimscan_version.restype = ctypes.c_char_p
             lib.vimscan_version.argtypes = []
+            lib.vimscan_ncssd_fwd.restype = ctypes.c_int
+            lib.vimscan_ncssd_fwd.argtypes = [vp] * 4 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
+            lib.vimscan_ncssd_plan.restype = ctypes.c_int
+            lib.vimscan_ncssd_plan.argtypes = [ctypes.POINTER(_Launch), ctypes.c_int64, ctypes.POINTER(_Plan)]
             _lib = lib
     return _lib
 
@@ -242,3 +247,73 @@ def fwd(x, dt, z, B, C, A, D, dt_bias, seg_len: int = 0, out=None, chunk_len: in
     """y = silu(z) * (C.h + D x) of the forward scan alone, on the GPU (vimscan_fwd); arguments as
     ``prepare_fwd``. Queued on torch's current stream; does not synchronise."""
     return prepare_fwd(x, dt, z, B, C, A, D, dt_bias, seg_len, out, chunk_len, general_decay, aux_swap, workspace)()
+
+
+def ncssd_info(batch, seqlen, d_inner, d_state=16, seg_len=0, io_dtype="bf16", chunk_len=0) -> dict:
+    """The library's plan for an NC-SSD call with this shape (host only; vimscan_ncssd_plan)."""
+    code = VIMSCAN_BF16 if io_dtype == "bf16" else VIMSCAN_F32
+    launch = make_launch(batch, seqlen, d_inner, d_state, code, chunk_len)
+    plan = _Plan()
+    _check(load_library().vimscan_ncssd_plan(ctypes.byref(launch), int(seg_len), ctypes.byref(plan)))
+    return {f: getattr(plan, f) for f, _ in _Plan._fields_}
+
+
+class PreparedNcssd:
+    """A validated NC-SSD call on fixed tensors (vimscan_ncssd_fwd): y = C (B^T (x . m)) per
+    sequence. x (B, L, Di); B, C (B, L, N) with N in {16, 32, 64}; x, B, C all float32 or all
+    bfloat16, contiguous, on one device; m (B, L) float32. seg_len: 0, or the length of the folded
+    sequences (must divide L). ``__call__`` only queues the kernels on the stream (torch's current
+    stream for x's device unless given)."""
+
+    def __init__(self, x, B, C, m, seg_len: int = 0, out=None, chunk_len: int = 0, workspace=None, stream=None):
+        lib = load_library()
+        if x.dim() != 3:
+            raise ValueError("x must be (batch, seqlen, d_inner)")
+        Bsz, L, Di = x.shape
+        N = B.shape[-1] if B.dim() == 3 else -1
+        dev = x.device
+        if dev.type != "cuda":
+            raise ValueError("inputs must be on a GPU device")
+        io = _io_code(x.dtype)
+        for t, shp in ((x, (Bsz, L, Di)), (B, (Bsz, L, N)), (C, (Bsz, L, N))):
+            if t.device != dev or t.dtype != x.dtype or tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError("x (B,L,Di) and B, C (B,L,N) must share device and dtype and be contiguous")
+        if m.device != dev or m.dtype != torch.float32 or tuple(m.shape) != (Bsz, L) or not m.is_contiguous():
+            raise ValueError("m must be a contiguous float32 (B, L) tensor on x's device")
+        if out is None:
+            out = torch.empty_like(x)
+        elif out.device != dev or out.dtype != x.dtype or out.shape != x.shape or not out.is_contiguous():
+            raise ValueError("out must match x")
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        launch = make_launch(Bsz, L, Di, N, io, chunk_len, False, 0, 0, stream)
+        plan = _Plan()
+        _check(lib.vimscan_ncssd_plan(ctypes.byref(launch), int(seg_len), ctypes.byref(plan)))
+        need = plan.workspace_bytes
+        if need > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            launch.workspace = workspace.data_ptr()
+            launch.workspace_bytes = workspace.numel() * workspace.element_size()
+        self.out = out
+        self.plan = {f: getattr(plan, f) for f, _ in _Plan._fields_}
+        self._keep = (x, B, C, m, out, workspace)
+        self._launch = launch
+        self._fn = lib.vimscan_ncssd_fwd
+        self._args = (x.data_ptr(), B.data_ptr(), C.data_ptr(), m.data_ptr(), int(seg_len), out.data_ptr(),
+                      ctypes.byref(launch))
+
+    def set_scan_events(self, ev0: int = 0, ev1: int = 0):
+        """hipEvent_t handles recorded before the first and after the last kernel of each call."""
+        self._launch.scan_events[0] = ev0 or None
+        self._launch.scan_events[1] = ev1 or None
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.out
+
+
+def ncssd_fwd(x, B, C, m, seg_len: int = 0, out=None, chunk_len: int = 0, workspace=None):
+    """NC-SSD global-state form y = C (B^T (x . m)) on the GPU (vimscan_ncssd_fwd); arguments as
+    ``PreparedNcssd``. Queued on torch's current stream; does not synchronise."""
+    return PreparedNcssd(x, B, C, m, seg_len, out, chunk_len, workspace)()

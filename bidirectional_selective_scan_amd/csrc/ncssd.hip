@@ -1,0 +1,534 @@
+// NC-SSD, the non-causal global-state form of state-space duality, for AMD MI355X (gfx950): HIP
+// kernels and the vimscan_ncssd_fwd / vimscan_ncssd_plan entry points of include/vimscan.h.
+//
+// What is computed (VSSD page, sections 4.2.3 to 4.2.5): per sequence of T tokens, with token
+// weights m_j (the reciprocal of the token's scalar transition),
+//     H = B^T (X . m)   [N x Di]   one hidden state shared by every token of the sequence
+//     Y = C H           [T x Di]   every token reads it out with its own C row
+// where X . m scales token j's row of X by m_j. Both are dense contractions with a short inner
+// (state) or outer (state) dimension, so they run on the matrix cores.
+//
+// Execution design (gfx950, wave64, MFMA 16x16 tiles):
+//  * A workgroup owns one sequence and 64 channels (k_ncssd_fused): its four waves take the
+//    sequence's 16-token tiles round-robin for the state, add their partial states through LDS
+//    in a fixed order, and read the state out for the same tiles: x is read once, y written
+//    once, H never leaves the chip. Long sequences with too few workgroups for the chip are
+//    split instead: pass 1 (k_ncssd_state) stores one partial state per token range, a small
+//    kernel (k_ncssd_reduce) adds them in range order into H in the workspace, and pass 2
+//    (k_ncssd_out) reads it out for groups of kOutTokens tokens. Results never depend on timing.
+//  * The state contraction of a wave, per 16-token tile: H += B'^T X with B' = B . m as the MFMA A operand
+//    (rows = states, K = tokens) and X as the B operand (K = tokens, columns =
+//    channels). Each lane reads its four consecutive channels of four consecutive tokens as
+//    plain 8-byte (bf16) or 16-byte (fp32) row loads, so X needs no transposition through LDS:
+//    the four MFMA column sets of a wave are the channels d0 + 4c + q, q = 0..3, and the lane
+//    regroups its loads into one operand per q.
+//  * The readout computes Y^T = H^T C^T: rows = channels, K = states, columns = 16
+//    tokens. The channel of MFMA q's row r is d0 + 16 (r / 4) + 4 q + (r % 4), so the four
+//    accumulators a lane ends with hold 16 consecutive channels of one token: y leaves as 16-byte
+//    stores. The H operand is loaded once per wave; per tile only the C rows are read.
+//  * bf16 io: X and C are exact bf16 MFMA operands. B . m and H are fp32 values; each is split
+//    into a bf16 high part and a bf16 remainder and both are multiplied (two MFMAs), so the
+//    contraction keeps about 16 significant bits on those operands and accumulates in fp32.
+//    fp32 io uses the fp32 MFMA (16x16x4) directly.
+//  * Sequences are split only when sequences x channel blocks is below about a thousand
+//    workgroups, so the chip has several thousand waves either way.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "vimscan.h"
+
+namespace {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;        // tokens per MFMA tile
+constexpr int kBlock = 64;       // channels per workgroup
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kOutTokens = 128;  // tokens per pass-2 workgroup
+constexpr int64_t kTargetWgs = 1024;
+
+struct NcArgs {
+    const void* x;   // [nseq * T][Di]
+    const void* B;   // [nseq * T][N]
+    const void* C;   // [nseq * T][N]
+    const float* m;  // [nseq * T]
+    void* y;         // [nseq * T][Di]
+    float* part;     // pass 1 output: [nseq][splits][N][Di] (the state itself when splits == 1)
+    float* H;        // [nseq][N][Di]
+    int T;           // tokens per sequence
+    int Di;
+    int splits;      // token ranges per sequence in pass 1
+    int span;        // tokens per range (a multiple of kTile)
+    int ncb;         // channel blocks of 64
+    int groups;      // token groups of kOutTokens per sequence in pass 2
+};
+
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+}
+__device__ __forceinline__ float from_bf16(uint32_t b) { return __uint_as_float(b << 16); }
+
+// v = hi + lo + O(2^-16 |v|), hi and lo bf16.
+struct HiLo {
+    short hi, lo;
+};
+__device__ __forceinline__ HiLo split_bf16(float v) {
+    const uint16_t h = to_bf16(v);
+    return {static_cast<short>(h), static_cast<short>(to_bf16(v - from_bf16(h)))};
+}
+
+template <typename IO> struct Io;
+template <> struct Io<float> { using elem = float; };
+template <> struct Io<uint16_t> { using elem = uint16_t; };
+
+__device__ __forceinline__ float ld_val(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_val(const uint16_t* p, int64_t i) { return from_bf16(p[i]); }
+
+// ---------------------------------------------------------------------------------------------
+// The state contraction of one wave: acc[q][nb] += B'^T X over the 16-token tiles t0 = tb +
+// 16 wave, tb + 16 (wave + 4), ... below te, for the 64 channels d0..d0+63. On return acc[q][nb][r]
+// is the state at n = 16 nb + 4 grp + r, channel d0 + 4 col + q (lane = 16 grp + col).
+
+template <typename IO, int NB>
+__device__ __forceinline__ void state_tiles(const NcArgs& a, int64_t row0, int d0, int tb, int te, int wave,
+                                            int lane, v4f (&acc)[4][NB]) {
+    constexpr int N = 16 * NB;
+    using E = typename Io<IO>::elem;
+    const E* x = static_cast<const E*>(a.x);
+    const E* Bm = static_cast<const E*>(a.B);
+    const int col = lane & 15, grp = lane >> 4;
+    const int dl = d0 + 4 * col;  // this lane's channels dl..dl+3 (all inside or all outside: Di % 16 == 0)
+    const bool dok = dl < a.Di;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[q][nb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int t0 = tb + wave * kTile; t0 < te; t0 += kWaves * kTile) {
+        if constexpr (sizeof(E) == 2) {
+            // K = 16 tokens: the lane supplies tokens t0 + 4 grp + e, e = 0..3
+            uint2 xr[4];
+            float mv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tok = t0 + 4 * grp + e;
+                const bool ok = tok < te;
+                xr[e] = (ok && dok) ? *reinterpret_cast<const uint2*>(x + (row0 + tok) * a.Di + dl) : make_uint2(0u, 0u);
+                mv[e] = ok ? a.m[row0 + tok] : 0.0f;
+            }
+            v4s bx[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bx[0][e] = static_cast<short>(xr[e].x & 0xffffu);
+                bx[1][e] = static_cast<short>(xr[e].x >> 16);
+                bx[2][e] = static_cast<short>(xr[e].y & 0xffffu);
+                bx[3][e] = static_cast<short>(xr[e].y >> 16);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                v4s ah, al;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = t0 + 4 * grp + e;
+                    const float bv = tok < te ? ld_val(Bm, (row0 + tok) * N + nb * 16 + col) * mv[e] : 0.0f;
+                    const HiLo hl = split_bf16(bv);
+                    ah[e] = hl.hi;
+                    al[e] = hl.lo;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[q][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bx[q], acc[q][nb], 0, 0, 0);
+                    acc[q][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bx[q], acc[q][nb], 0, 0, 0);
+                }
+            }
+        } else {
+            // four K = 4 steps: step k's lane supplies token t0 + 4 k + grp
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int tok = t0 + 4 * k + grp;
+                const bool ok = tok < te;
+                const float4 xv = (ok && dok) ? *reinterpret_cast<const float4*>(x + (row0 + tok) * a.Di + dl)
+                                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const float mv = ok ? a.m[row0 + tok] : 0.0f;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float bv = ok ? ld_val(Bm, (row0 + tok) * N + nb * 16 + col) * mv : 0.0f;
+                    acc[0][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.x, acc[0][nb], 0, 0, 0);
+                    acc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.y, acc[1][nb], 0, 0, 0);
+                    acc[2][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.z, acc[2][nb], 0, 0, 0);
+                    acc[3][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.w, acc[3][nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Every wave's state contraction into LDS: red[wave][n][c] holds channels d0 + 4c + 0..3.
+template <int NB>
+__device__ __forceinline__ void park_state(float4 (*red)[16 * NB][kBlock / 4], int wave, int lane,
+                                           const v4f (&acc)[4][NB]) {
+    const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            red[wave][nb * 16 + 4 * grp + r][col] = make_float4(acc[0][nb][r], acc[1][nb][r], acc[2][nb][r], acc[3][nb][r]);
+}
+
+// The readout of one wave: y = C H for the 16-token tiles i0 = gb + 16 wave, gb + 16 (wave + 4),
+// ... below ge and the 64 channels d0..d0+63. hval(n, c) returns the state at n for channel
+// d0 + c. MFMA q's row r is channel d0 + 16 (r / 4) + 4 q + (r % 4): as the A operand this
+// lane supplies row col; as the output it holds rows 4 grp + 0..3, i.e. 16 consecutive channels
+// d0 + 16 grp + 0..15 of token i0 + col.
+template <typename IO, int NB, typename HVal>
+__device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0, int gb, int ge, int wave, int lane,
+                                          HVal hval) {
+    constexpr int N = 16 * NB;
+    using E = typename Io<IO>::elem;
+    const E* Cm = static_cast<const E*>(a.C);
+    E* y = static_cast<E*>(a.y);
+    const int col = lane & 15, grp = lane >> 4;
+    const int arow = 16 * (col >> 2) + (col & 3);  // channel of A row col in MFMA 0, less d0
+    const bool aok = d0 + 16 * (col >> 2) < a.Di;
+    const int dout = d0 + 16 * grp;
+    const bool ook = dout < a.Di;
+
+    if constexpr (sizeof(E) == 2) {
+        v4s ah[4][NB], al[4][NB];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float h = aok ? hval(nb * 16 + 4 * grp + e, arow + 4 * q) : 0.0f;
+                    const HiLo hl = split_bf16(h);
+                    ah[q][nb][e] = hl.hi;
+                    al[q][nb][e] = hl.lo;
+                }
+        for (int i0 = gb + wave * kTile; i0 < ge; i0 += kWaves * kTile) {
+            const int tok = i0 + col;  // this lane's token as the B operand and in the output
+            const bool tok_ok = tok < ge;
+            v4f acc[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const uint2 cr = tok_ok ? *reinterpret_cast<const uint2*>(Cm + (row0 + tok) * N + nb * 16 + 4 * grp)
+                                        : make_uint2(0u, 0u);
+                v4s bc;
+                bc[0] = static_cast<short>(cr.x & 0xffffu);
+                bc[1] = static_cast<short>(cr.x >> 16);
+                bc[2] = static_cast<short>(cr.y & 0xffffu);
+                bc[3] = static_cast<short>(cr.y >> 16);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah[q][nb], bc, acc[q], 0, 0, 0);
+                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al[q][nb], bc, acc[q], 0, 0, 0);
+                }
+            }
+            if (tok_ok && ook) {
+                uint32_t w[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    w[2 * q] = static_cast<uint32_t>(to_bf16(acc[q][0])) | (static_cast<uint32_t>(to_bf16(acc[q][1])) << 16);
+                    w[2 * q + 1] = static_cast<uint32_t>(to_bf16(acc[q][2])) | (static_cast<uint32_t>(to_bf16(acc[q][3])) << 16);
+                }
+                uint4* dst = reinterpret_cast<uint4*>(y + (row0 + tok) * a.Di + dout);
+                dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            }
+        }
+    } else {
+        // K = 4 steps: step k's lane supplies state n = 16 nb + 4 k + grp
+        float ha[4][NB][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ha[q][nb][k] = aok ? hval(nb * 16 + 4 * k + grp, arow + 4 * q) : 0.0f;
+        for (int i0 = gb + wave * kTile; i0 < ge; i0 += kWaves * kTile) {
+            const int tok = i0 + col;
+            const bool tok_ok = tok < ge;
+            v4f acc[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float cv = tok_ok ? Cm[(row0 + tok) * N + nb * 16 + 4 * k + grp] : 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[q][nb][k], cv, acc[q], 0, 0, 0);
+                }
+            if (tok_ok && ook) {
+                float4* dst = reinterpret_cast<float4*>(y + (row0 + tok) * a.Di + dout);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Whole sequence in one workgroup (the sequence is not split): the state is summed in LDS and
+// read out at once; it never goes to memory. One workgroup per (channel block, sequence), channel
+// block fastest.
+
+template <typename IO, int NB>
+__global__ __launch_bounds__(256) void k_ncssd_fused(NcArgs a) {
+    constexpr int N = 16 * NB;
+    __shared__ float4 red[kWaves][N][kBlock / 4];
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int d0 = static_cast<int>(blockIdx.x % a.ncb) * kBlock;
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x / a.ncb) * a.T;
+    v4f acc[4][NB];
+    state_tiles<IO, NB>(a, row0, d0, 0, a.T, wave, lane, acc);
+    park_state<NB>(red, wave, lane, acc);
+    __syncthreads();
+    const float* rf = reinterpret_cast<const float*>(&red[0][0][0]);
+    out_tiles<IO, NB>(a, row0, d0, 0, a.T, wave, lane, [&](int n, int c) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += rf[(w * N + n) * kBlock + c];  // waves in a fixed order
+        return v;
+    });
+}
+
+// Pass 1 of a split sequence: the partial state of one token range. One workgroup per (channel
+// block, range, sequence), in that order of speed.
+template <typename IO, int NB>
+__global__ __launch_bounds__(256) void k_ncssd_state(NcArgs a) {
+    constexpr int N = 16 * NB;
+    __shared__ float4 red[kWaves][N][kBlock / 4];
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int d0 = static_cast<int>(blockIdx.x % a.ncb) * kBlock;
+    const int split = static_cast<int>((blockIdx.x / a.ncb) % a.splits);
+    const int s = static_cast<int>(blockIdx.x / a.ncb / a.splits);
+    const int tb = split * a.span;
+    const int te = min(tb + a.span, a.T);
+    v4f acc[4][NB];
+    state_tiles<IO, NB>(a, static_cast<int64_t>(s) * a.T, d0, tb, te, wave, lane, acc);
+    park_state<NB>(red, wave, lane, acc);
+    __syncthreads();
+    // 256 threads add the four waves' blocks (N x 16 float4) and store them
+    float* dst = a.part + (static_cast<int64_t>(s) * a.splits + split) * N * a.Di + d0;
+    for (int i = static_cast<int>(threadIdx.x); i < N * (kBlock / 4); i += kBlock * kWaves) {
+        const int n = i / (kBlock / 4), c = i % (kBlock / 4);
+        if (d0 + 4 * c >= a.Di) continue;
+        float4 v = red[0][n][c];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            const float4 o = red[w][n][c];
+            v.x += o.x;
+            v.y += o.y;
+            v.z += o.z;
+            v.w += o.w;
+        }
+        *reinterpret_cast<float4*>(dst + static_cast<int64_t>(n) * a.Di + 4 * c) = v;
+    }
+}
+
+// Sum of the split partial states, in split order. One thread per 4 values of H.
+__global__ __launch_bounds__(256) void k_ncssd_reduce(NcArgs a, int64_t quads, int nd) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= quads) return;
+    const int64_t s = i / (nd / 4), r = i % (nd / 4);  // nd = N * Di values per sequence
+    const float4* src = reinterpret_cast<const float4*>(a.part + s * a.splits * nd) + r;
+    float4 v = src[0];
+    for (int k = 1; k < a.splits; ++k) {
+        const float4 o = src[static_cast<int64_t>(k) * (nd / 4)];
+        v.x += o.x;
+        v.y += o.y;
+        v.z += o.z;
+        v.w += o.w;
+    }
+    reinterpret_cast<float4*>(a.H + s * nd)[r] = v;
+}
+
+// Pass 2 of a split sequence: y = C H for kOutTokens tokens x 64 channels, H from memory. One
+// workgroup per (channel block, token group, sequence), in that order of speed.
+template <typename IO, int NB>
+__global__ __launch_bounds__(256) void k_ncssd_out(NcArgs a) {
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int d0 = static_cast<int>(blockIdx.x % a.ncb) * kBlock;
+    const int gb = static_cast<int>((blockIdx.x / a.ncb) % a.groups) * kOutTokens;
+    const int s = static_cast<int>(blockIdx.x / a.ncb / a.groups);
+    const int ge = min(gb + kOutTokens, a.T);
+    const float* Hs = a.H + static_cast<int64_t>(s) * 16 * NB * a.Di + d0;
+    const int Di = a.Di;
+    out_tiles<IO, NB>(a, static_cast<int64_t>(s) * a.T, d0, gb, ge, wave, lane,
+                      [&](int n, int c) { return Hs[static_cast<int64_t>(n) * Di + c]; });
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side
+
+struct NcPlan {
+    int64_t nseq, T, splits, span, ncb, groups, N;
+    size_t off_H, ws;
+};
+
+bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) % al) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && a0 < b0 + nb && b0 < a0 + na;
+}
+
+int nc_plan(const vimscan_launch* l, int64_t seg_len, NcPlan* p) {
+    if (!l) return VIMSCAN_ERR_NULL;
+    if (l->batch < 0 || l->seqlen < 0 || l->d_inner < 0) return VIMSCAN_ERR_SHAPE;
+    if (l->d_state != 16 && l->d_state != 32 && l->d_state != 64) return VIMSCAN_ERR_SHAPE;
+    if (l->d_inner % 16 != 0 || l->d_inner >= (int64_t(1) << 22)) return VIMSCAN_ERR_SHAPE;
+    const int64_t lim = int64_t(1) << 31;
+    if (l->batch > 0 && l->seqlen > 0 && l->d_inner > 0) {
+        if (l->seqlen > lim / l->batch) return VIMSCAN_ERR_SHAPE;
+        const int64_t bl = l->batch * l->seqlen;
+        if (l->d_inner >= lim / bl + 1 || bl * l->d_inner >= lim) return VIMSCAN_ERR_SHAPE;
+    }
+    if (l->io_dtype != VIMSCAN_F32 && l->io_dtype != VIMSCAN_BF16) return VIMSCAN_ERR_DTYPE;
+    if (seg_len < 0 || (seg_len > 0 && l->seqlen % seg_len != 0)) return VIMSCAN_ERR_SEGLEN;
+    if (l->chunk_len < 0) return VIMSCAN_ERR_CHUNK;
+    if (l->flags != 0) return VIMSCAN_ERR_FLAGS;
+    std::memset(p, 0, sizeof(*p));
+    p->N = l->d_state;
+    if (l->batch == 0 || l->seqlen == 0 || l->d_inner == 0) return VIMSCAN_OK;
+    p->T = seg_len > 0 ? seg_len : l->seqlen;
+    p->nseq = l->batch * (l->seqlen / p->T);
+    p->ncb = (l->d_inner + kBlock - 1) / kBlock;
+    const int64_t quantum = kTile * kWaves;  // one tile per wave
+    int64_t span;
+    if (l->chunk_len > 0) {
+        span = (l->chunk_len + kTile - 1) / kTile * kTile;
+    } else {
+        // Split long sequences until the pass has about kTargetWgs workgroups, keeping at least
+        // two tiles per wave.
+        const int64_t wgs = p->nseq * p->ncb;
+        int64_t k = wgs >= kTargetWgs ? 1 : (kTargetWgs + wgs - 1) / wgs;
+        const int64_t kmax = (p->T + 2 * quantum - 1) / (2 * quantum);
+        if (k > kmax) k = kmax;
+        if (k < 1) k = 1;
+        span = (p->T + k - 1) / k;
+        span = (span + quantum - 1) / quantum * quantum;
+    }
+    if (span >= p->T) span = (p->T + kTile - 1) / kTile * kTile;
+    p->span = span;
+    p->splits = (p->T + span - 1) / span;
+    p->groups = (p->T + kOutTokens - 1) / kOutTokens;
+    if (p->splits > 1) {  // split partial states, then H
+        const size_t hsz = static_cast<size_t>(p->nseq) * p->N * l->d_inner * sizeof(float);
+        p->off_H = (hsz * static_cast<size_t>(p->splits) + 255) / 256 * 256;
+        p->ws = p->off_H + hsz;
+    }
+    return VIMSCAN_OK;
+}
+
+template <typename IO, int NB>
+int nc_launch(const NcArgs& a, const NcPlan& p, hipStream_t s) {
+    const dim3 block(kBlock * kWaves);
+    if (p.splits == 1) {
+        hipLaunchKernelGGL((k_ncssd_fused<IO, NB>), dim3(static_cast<unsigned>(p.ncb * p.nseq)), block, 0, s, a);
+        return hipGetLastError() == hipSuccess ? VIMSCAN_OK : VIMSCAN_ERR_HIP;
+    }
+    hipLaunchKernelGGL((k_ncssd_state<IO, NB>), dim3(static_cast<unsigned>(p.ncb * p.splits * p.nseq)), block, 0, s, a);
+    const int nd = static_cast<int>(p.N * a.Di);
+    const int64_t quads = p.nseq * nd / 4;
+    hipLaunchKernelGGL(k_ncssd_reduce, dim3(static_cast<unsigned>((quads + 255) / 256)), dim3(256), 0, s, a, quads, nd);
+    hipLaunchKernelGGL((k_ncssd_out<IO, NB>), dim3(static_cast<unsigned>(p.ncb * p.groups * p.nseq)), block, 0, s, a);
+    return hipGetLastError() == hipSuccess ? VIMSCAN_OK : VIMSCAN_ERR_HIP;
+}
+
+template <typename IO>
+int nc_dispatch(const NcArgs& a, const NcPlan& p, hipStream_t s) {
+    switch (p.N) {
+        case 16: return nc_launch<IO, 1>(a, p, s);
+        case 32: return nc_launch<IO, 2>(a, p, s);
+        default: return nc_launch<IO, 4>(a, p, s);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int vimscan_ncssd_plan(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan) {
+    if (!plan) return VIMSCAN_ERR_NULL;
+    NcPlan p;
+    const int rc = nc_plan(launch, seg_len, &p);
+    if (rc != VIMSCAN_OK) return rc;
+    plan->sequences = p.nseq;
+    plan->seq_tokens = p.T;
+    plan->chunk_len = p.span;
+    plan->chunks = p.splits;
+    plan->workgroups = p.nseq * p.ncb * p.splits;
+    plan->kernels = p.nseq == 0 ? 0 : (p.splits > 1 ? 3 : 1);
+    plan->park_in_workspace = 0;
+    plan->workspace_bytes = p.ws;
+    return VIMSCAN_OK;
+}
+
+int vimscan_ncssd_fwd(const void* x, const void* B, const void* C, const float* m, int64_t seg_len, void* y,
+                      const vimscan_launch* launch) {
+    if (!launch) return VIMSCAN_ERR_NULL;
+    NcPlan p;
+    const int rc = nc_plan(launch, seg_len, &p);
+    if (rc != VIMSCAN_OK) return rc;
+    if (launch->batch == 0 || launch->seqlen == 0 || launch->d_inner == 0) return VIMSCAN_OK;
+    if (!x || !B || !C || !m || !y) return VIMSCAN_ERR_NULL;
+    const bool bf = launch->io_dtype == VIMSCAN_BF16;
+    const size_t e = bf ? 2 : 4;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(B, e) || !aligned(C, bf ? 8 : 4) || !aligned(m, 4))
+        return VIMSCAN_ERR_ALIGN;
+    const size_t tokens = static_cast<size_t>(launch->batch) * launch->seqlen;
+    const size_t ny = tokens * launch->d_inner * e;
+    const struct {
+        const void* p;
+        size_t n;
+    } ins[] = {{x, ny}, {B, tokens * p.N * e}, {C, tokens * p.N * e}, {m, tokens * 4}};
+    for (const auto& in : ins)
+        if (overlaps(y, ny, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
+    if (p.ws > 0) {
+        if (!launch->workspace || launch->workspace_bytes < p.ws) return VIMSCAN_ERR_WORKSPACE;
+        if (!aligned(launch->workspace, 16)) return VIMSCAN_ERR_ALIGN;
+        if (overlaps(y, ny, launch->workspace, p.ws)) return VIMSCAN_ERR_ALIAS;
+        for (const auto& in : ins)
+            if (overlaps(launch->workspace, p.ws, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
+    }
+
+    NcArgs a;
+    a.x = x;
+    a.B = B;
+    a.C = C;
+    a.m = m;
+    a.y = y;
+    char* ws = static_cast<char*>(launch->workspace);
+    a.H = p.splits > 1 ? reinterpret_cast<float*>(ws + p.off_H) : nullptr;
+    a.part = p.splits > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+    a.T = static_cast<int>(p.T);
+    a.Di = static_cast<int>(launch->d_inner);
+    a.splits = static_cast<int>(p.splits);
+    a.span = static_cast<int>(p.span);
+    a.ncb = static_cast<int>(p.ncb);
+    a.groups = static_cast<int>(p.groups);
+    hipStream_t s = static_cast<hipStream_t>(launch->stream);
+    hipEvent_t ev0 = static_cast<hipEvent_t>(launch->scan_events[0]);
+    hipEvent_t ev1 = static_cast<hipEvent_t>(launch->scan_events[1]);
+    const bool timed = ev0 && ev1;
+    if (timed && hipEventRecord(ev0, s) != hipSuccess) return VIMSCAN_ERR_HIP;
+    const int lr = bf ? nc_dispatch<uint16_t>(a, p, s) : nc_dispatch<float>(a, p, s);
+    if (lr != VIMSCAN_OK) return lr;
+    if (timed && hipEventRecord(ev1, s) != hipSuccess) return VIMSCAN_ERR_HIP;
+    return VIMSCAN_OK;
+}
+
+}  // extern "C"

@@ -89,7 +89,7 @@ typedef struct vimscan_launch {
     int64_t batch;          /* B >= 0 */
     int64_t seqlen;         /* L >= 0 (the folded stream length when seg_len > 0) */
     int64_t d_inner;        /* Di >= 0 */
-    int64_t d_state;        /* N; must be 16 */
+    int64_t d_state;        /* N; 16 for the scans; 16, 32 or 64 for vimscan_ncssd_fwd */
     int32_t io_dtype;       /* enum vimscan_io_dtype */
     int32_t flags;          /* VIMSCAN_FLAG_* bits */
     int64_t chunk_len;      /* 0: the library picks; > 0: tokens per chunk of the chunked scan
@@ -186,6 +186,38 @@ int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* 
 int vimscan_fwd(const void* x, const void* dt, const void* z, const void* B, const void* C,
                 const float* A, const float* D, const float* dt_bias, int64_t seg_len, void* y,
                 const vimscan_launch* launch);
+
+/*
+ * NC-SSD, the non-causal global-state form of state-space duality (VSSD page, sections 4.2.3 to
+ * 4.2.5): the SSD recurrence divided by each token's scalar transition A_j, summed over both
+ * scan directions and without the token's own term, leaves one hidden state per sequence that
+ * every token reads out:
+ *   H[n][d] = sum_j B[j][n] * m[j] * x[j][d],   y[i][d] = sum_n C[i][n] * H[n][d]
+ * i.e. y = C (B^T (x . m)) per sequence, with m[j] = 1 / A_j the weight of token j. With
+ * seg_len > 0 every segment of seg_len tokens is its own sequence with its own H (folding).
+ *
+ * Layouts (row-major, dense): x, y [batch][seqlen][d_inner] io dtype; B, C
+ * [batch][seqlen][d_state] io dtype; m [batch][seqlen] fp32. launch->d_state is N (16, 32 or
+ * 64); d_inner must be a multiple of 16; flags must be 0 (VIMSCAN_ERR_FLAGS); chunk_len > 0
+ * sets the tokens of a sequence that one workgroup of the state pass sums (rounded up to a
+ * multiple of 16; 0: the library picks); scan_events, when set, are recorded before the first
+ * and after the last kernel. x and y must be 16-byte aligned, B aligned to its element size, C to
+ * 8 bytes (bf16) or 4 (fp32), m to 4 (VIMSCAN_ERR_ALIGN). When one workgroup covers a whole
+ * sequence, H stays on the chip and no workspace is needed; when long sequences are split
+ * (vimscan_ncssd_plan: chunks > 1) the workspace holds the split partial states and H. fp32 io runs the fp32 matrix-core contraction; bf16 io multiplies the
+ * exact bf16 x and C by B*m and H each split into two bf16 parts, accumulating in fp32. Same
+ * ownership, stream, aliasing and empty-shape rules as vimscan_bidir_fwd; VIMSCAN_ERR_SHAPE also
+ * for d_state outside {16, 32, 64} or d_inner % 16 != 0.
+ */
+int vimscan_ncssd_fwd(const void* x, const void* B, const void* C, const float* m, int64_t seg_len,
+                      void* y, const vimscan_launch* launch);
+
+/* Plan of a vimscan_ncssd_fwd call: sequences, seq_tokens; chunk_len = tokens per state-pass
+   workgroup, chunks = workgroups per sequence and channel block in that pass; workgroups of the
+   state pass; kernels (1 when a sequence is not split: state and readout in one kernel; 3 when
+   it is: partial states, their sum, readout); workspace_bytes (0 when not split). Host only. Returns VIMSCAN_OK or the error the call would
+   return. */
+int vimscan_ncssd_plan(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan);
 
 /* Fills *plan for a call with this launch and seg_len (workspace fields of launch are
    ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */

@@ -276,3 +276,73 @@ def test_forward_only_arguments(lib):
     # y overlapping B (2*12*16 fp32)
     p = [0x10000000 * (j + 1) for j in range(8)]
     assert _call_fwd(lib, _launch(), p, y=p[3] + 64) == ALIAS
+
+
+def test_ncssd_plans(lib):
+    v = binding.ncssd_info(128, 197, 768, 16, 0, "bf16")
+    # one workgroup per (sequence, 64 channels) holds the whole sequence: one kernel, no workspace
+    assert (v["chunks"], v["kernels"], v["workgroups"], v["workspace_bytes"]) == (1, 1, 128 * 12, 0)
+    f = binding.ncssd_info(1, 256 * 51, 1536, 16, 51, "bf16")
+    assert (f["sequences"], f["seq_tokens"], f["kernels"], f["workspace_bytes"]) == (256, 51, 1, 0)
+    h = binding.ncssd_info(8, 1025, 768, 16, 0, "bf16")
+    # 96 (sequence, channel block) pairs are too few: the sequences are split
+    assert h["chunks"] > 1 and h["kernels"] == 3 and h["chunk_len"] % 64 == 0
+    assert h["chunks"] == -(-1025 // h["chunk_len"])
+    hsz = 8 * 16 * 768 * 4
+    assert h["workspace_bytes"] == -(-hsz * h["chunks"] // 256) * 256 + hsz
+    c = binding.ncssd_info(2, 65, 32, 64, 0, "f32", chunk_len=20)   # rounded up to 32 tokens
+    assert (c["chunk_len"], c["chunks"], c["kernels"]) == (32, 3, 3)
+    assert c["workspace_bytes"] == 3 * 2 * 64 * 32 * 4 + 2 * 64 * 32 * 4
+    assert binding.ncssd_info(2, 65, 32, 32, 0, "f32", chunk_len=1000)["chunks"] == 1
+
+
+def _nc_launch(**kw):
+    base = dict(batch=2, seqlen=12, d_inner=64, d_state=16, io_dtype=binding.VIMSCAN_F32, chunk_len=0,
+                general_decay=False, workspace=0, workspace_bytes=0, stream=0)
+    base.update(kw)
+    return binding.make_launch(**base)
+
+
+def _nc_plan(lib, launch, seg_len=0):
+    plan = binding._Plan()
+    return lib.vimscan_ncssd_plan(ctypes.byref(launch) if launch is not None else None, seg_len, ctypes.byref(plan))
+
+
+@pytest.mark.parametrize("kw,code", [(dict(d_state=8), SHAPE), (dict(d_state=48), SHAPE), (dict(d_inner=40), SHAPE),
+                                     (dict(batch=-1), SHAPE), (dict(io_dtype=7), DTYPE), (dict(chunk_len=-1), CHUNK),
+                                     (dict(general_decay=True), FLAGS), (dict(d_state=64), OK), (dict(d_state=32), OK)])
+def test_ncssd_plan_rejects_bad_launches(lib, kw, code):
+    assert _nc_plan(lib, _nc_launch(**kw)) == code
+
+
+def _call_nc(lib, launch, ptrs=None, seg_len=0, y=None):
+    p = ptrs or [0x10000000 * (i + 1) for i in range(4)]
+    y = 0x7F0000000 if y is None else y
+    return lib.vimscan_ncssd_fwd(*p, seg_len, y, ctypes.byref(launch) if launch is not None else None)
+
+
+def test_ncssd_arguments(lib):
+    assert _call_nc(lib, None) == NULL
+    assert _nc_plan(lib, None) == NULL
+    assert _call_nc(lib, _nc_launch(seqlen=12), seg_len=5) == SEGLEN
+    assert _nc_plan(lib, _nc_launch(seqlen=12), seg_len=5) == SEGLEN
+    for i in range(4):
+        p = [0x10000000 * (j + 1) for j in range(4)]
+        p[i] = 0
+        assert _call_nc(lib, _nc_launch(), p) == NULL
+    assert _call_nc(lib, _nc_launch(), y=0) == NULL
+    assert _call_nc(lib, _nc_launch(batch=0), [0] * 4, y=0) == OK
+    # x and y need 16 bytes; bf16 C needs 8; fp32 B and m need 4
+    for i, off in ((0, 8), (2, 4), (1, 2), (3, 2)):
+        p = [0x10000000 * (j + 1) for j in range(4)]
+        p[i] += off
+        assert _call_nc(lib, _nc_launch(io_dtype=binding.VIMSCAN_BF16 if i == 2 else binding.VIMSCAN_F32), p) == ALIGN
+    assert _call_nc(lib, _nc_launch(), y=0x7F0000008) == ALIGN
+    # y overlapping x, or m
+    p = [0x10000000 * (j + 1) for j in range(4)]
+    assert _call_nc(lib, _nc_launch(), p, y=p[0] + 256) == ALIAS
+    assert _call_nc(lib, _nc_launch(), p, y=p[3] - 64) == ALIAS
+    # a split plan needs its workspace
+    assert _call_nc(lib, _nc_launch(seqlen=64, chunk_len=16)) == WORKSPACE
+    launch = _nc_launch(seqlen=64, chunk_len=16, workspace=0x50000000, workspace_bytes=16)
+    assert _call_nc(lib, launch) == WORKSPACE
