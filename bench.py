@@ -8,8 +8,10 @@ inputs (more than the 256 MB Infinity Cache holds), so every step reads its inpu
 
 Also reported: the dominant kernel's ALU roofline (the scan's exponentials and fp32 arithmetic
 bind before HBM does; that kernel is timed alone with HIP events the library records around it),
-the same path with the per-state exponential forced (general_decay), and the float64 CPU oracle
-timed on this host's cores.
+the same path with the per-state exponential forced (general_decay), the directional convolution
+fused in front (conv_fused), the forward-only scan with and without the auxiliary-token swap, the
+NC-SSD global-state form on the same shape (ncssd: an HBM roofline, on the matrix cores), and the
+float64 CPU oracle timed on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 """
@@ -36,6 +38,9 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 CACHE_BYTES = 256 * 2 ** 20   # Infinity Cache
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_vim_s.json")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_selective_scan_amd", "csrc", "vimscan.hip")
+NCSSD_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_ncssd_vim_s.json")
+NCSSD_SOURCE = os.path.join(ROOT, "bidirectional_selective_scan_amd", "csrc", "ncssd.hip")
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks, published
 
 # ALU work of the scan per (batch, token, channel), in fp32 VALU lane-operations: an FMA,
 # multiply, add, compare or select is one; a transcendental (exp2, log2, rcp) counts two: on the
@@ -62,18 +67,18 @@ def alu_ops_per_element(geometric: bool) -> float:
     return ops + TRANS_OPS * trans
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(path: str = KERNEL_SOURCE) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """Per-launch HBM traffic of the main scan kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def load_traffic(workload: str, path: str = PROFILE_TRAFFIC, source: str = KERNEL_SOURCE):
+    """Per-launch HBM traffic of a kernel from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
     try:
-        rec = json.load(open(PROFILE_TRAFFIC))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256_16") != kernel_source_hash(source):
         return None
     return rec.get("bytes_per_launch")
 
@@ -105,6 +110,28 @@ def cpu_baseline(inp: dict, w) -> dict:
                       f"({round(3 * t * cores, 1)} core-seconds in all)"}
 
 
+def ncssd_leg(w, timed, stats_us, plan, nbytes, ncopies) -> dict:
+    """The NC-SSD global-state form y = C (B^T (x . m)) on the workload's shape: HBM roofline of
+    the call (its kernels bracketed by the library's events) and the matrix-core rate."""
+    wall, per_call, per_kern = timed("ncssd")
+    k = float(np.mean(per_kern))
+    flops = 2 * 2 * w.tokens_channels * 16   # state B^T (x . m) and readout C H, N = 16
+    peak = MFMA_PEAK_TFLOPS[w.io_dtype]
+    gbs = nbytes / k / 1e9
+    kernel = "k_ncssd_fused" if plan["chunks"] == 1 else "k_ncssd_state + k_ncssd_reduce + k_ncssd_out"
+    return {"what": "NC-SSD global-state form y = C (B^T (x . m)), N = 16 (vimscan_ncssd_fwd)",
+            "value": round(nbytes * len(per_call) / wall / 1e9, 2), "unit": "GB/s",
+            "call_us": stats_us(per_call), "kernel_us": round(k * 1e6, 3), "kernels_per_step": plan["kernels"],
+            "input_copies": ncopies, "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": kernel,
+                         "traffic": load_traffic(w.name, NCSSD_TRAFFIC, NCSSD_SOURCE)},
+            "mfma": {"achieved": round(flops / k / 1e12, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / k / 1e12 / peak, 5),
+                     "basis": "algorithmic flops 4 x tokens x channels x N; the bf16 path issues twice that "
+                              "(high and low parts of B*m and H)"}}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +144,9 @@ def main(argv=None):
                     help="skip the measurement with the directional convolution (4 taps) in front of the scan")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only scan measurements (with and without the auxiliary swap)")
+    ap.add_argument("--no-ncssd", action="store_true", help="skip the NC-SSD global-state form measurement")
+    ap.add_argument("--only-ncssd", action="store_true",
+                    help="measure only the NC-SSD global-state form (for its counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte buffer 5 times (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -169,6 +199,21 @@ def main(argv=None):
                                            params[0], params[2], params[4], seg_len=w.seg_len, out=outs[i],
                                            aux_swap=swap) for i in range(ncopy)]
 
+    # NC-SSD on inputs of the same shape: x, B, C in the io dtype, m fp32
+    from bidirectional_selective_scan_amd.inputs import ncssd_inputs
+    nci = ncssd_inputs(w.batch, w.seqlen, w.d_inner, 16, w.io_dtype, w.seed)
+    e_io = 2 if w.io_dtype == "bf16" else 4
+    nc_bytes = 2 * w.tokens_channels * e_io + 2 * w.batch * w.seqlen * 16 * e_io + w.batch * w.seqlen * 4
+    nc_copies = max(2, -(-2 * CACHE_BYTES // nc_bytes) + 1)
+    nc_base = {k: torch.from_numpy(nci[k]).to(dev) for k in ("x", "B", "C", "m")}
+    for k in ("x", "B", "C"):
+        nc_base[k] = nc_base[k].to(tdt)
+    calls["ncssd"] = []
+    for i in range(nc_copies):
+        t = {k: v.clone() for k, v in nc_base.items()}
+        calls["ncssd"].append(binding.PreparedNcssd(t["x"], t["B"], t["C"], t["m"], seg_len=w.seg_len,
+                                                    out=torch.empty_like(t["x"])))
+
     stream = torch.cuda.current_stream(dev)
 
     def make_events(n):
@@ -181,6 +226,7 @@ def main(argv=None):
 
     def timed(which):   # False: automatic transitions, True: forced general, "conv": with the convolution
         cl = calls[which]
+        ncopy = len(cl)
         for i in range(args.warmup):
             cl[i % ncopy]()
         torch.cuda.synchronize(dev)
@@ -205,6 +251,10 @@ def main(argv=None):
         return {"median": round(float(np.median(v)) * 1e6, 3), "min": round(float(np.min(v)) * 1e6, 3),
                 "p90": round(float(np.percentile(v, 90)) * 1e6, 3), "mean": round(float(np.mean(v)) * 1e6, 3)}
 
+    if args.only_ncssd:
+        print(json.dumps({"ncssd": ncssd_leg(w, timed, stats_us, calls["ncssd"][0].plan, nc_bytes, nc_copies)}),
+              flush=True)
+        return 0
     wall, per_call, per_scan = timed(False)
     ms_per_step = wall / args.steps * 1e3
     value = nbytes * args.steps / wall / 1e9
@@ -277,6 +327,8 @@ def main(argv=None):
                                                                          if name == "fwd_swap" else ""),
                           "value": round(fbytes * args.steps / wall_f / 1e9, 2), "unit": "GB/s",
                           "call_us": stats_us(per_call_f), "kernel_us": round(float(np.mean(per_scan_f)) * 1e6, 3)}
+    if not args.no_ncssd:
+        out["ncssd"] = ncssd_leg(w, timed, stats_us, calls["ncssd"][0].plan, nc_bytes, nc_copies)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out), flush=True)

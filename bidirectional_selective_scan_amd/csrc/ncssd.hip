@@ -37,6 +37,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "vimscan.h"
 
@@ -50,6 +51,9 @@ constexpr int kBlock = 64;       // channels per workgroup
 constexpr int kWaves = 4;        // waves per workgroup
 constexpr int kOutTokens = 128;  // tokens per pass-2 workgroup
 constexpr int64_t kTargetWgs = 1024;
+constexpr int kStageRow = 36;   // words per token row of a wave's bf16 output tile in LDS (32 + 4 pad)
+constexpr int kStageRowF = 68;  // the same for fp32 (64 + 4 pad)
+template <typename IO> constexpr int kStageWords = kTile * (sizeof(IO) == 2 ? kStageRow : kStageRowF);  // per wave
 
 struct NcArgs {
     const void* x;   // [nseq * T][Di]
@@ -81,6 +85,16 @@ __device__ __forceinline__ HiLo split_bf16(float v) {
     return {static_cast<short>(h), static_cast<short>(to_bf16(v - from_bf16(h)))};
 }
 
+// Logical workgroup id for hardware id i of n: the hardware deals workgroups to the 8 XCDs
+// round-robin; this gives each XCD one contiguous range of logical ids, so the channel blocks of
+// one sequence (consecutive logical ids) share an L2 and fetch that sequence's B, C and m rows
+// from memory once.
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = i & 7, k = i >> 3;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
 template <typename IO> struct Io;
 template <> struct Io<float> { using elem = float; };
 template <> struct Io<uint16_t> { using elem = uint16_t; };
@@ -92,76 +106,99 @@ __device__ __forceinline__ float ld_val(const uint16_t* p, int64_t i) { return f
 // The state contraction of one wave: acc[q][nb] += B'^T X over the 16-token tiles t0 = tb +
 // 16 wave, tb + 16 (wave + 4), ... below te, for the 64 channels d0..d0+63. On return acc[q][nb][r]
 // is the state at n = 16 nb + 4 grp + r, channel d0 + 4 col + q (lane = 16 grp + col).
+// Tiles are taken kGroup<NB> at a time: every load of a group is issued before any of its
+// arithmetic, so a wave waits for memory once per group rather than once per tile.
+
+template <int NB> constexpr int kGroup = NB >= 4 ? 2 : 1;
 
 template <typename IO, int NB>
 __device__ __forceinline__ void state_tiles(const NcArgs& a, int64_t row0, int d0, int tb, int te, int wave,
                                             int lane, v4f (&acc)[4][NB]) {
     constexpr int N = 16 * NB;
+    constexpr int G = kGroup<NB>;
     using E = typename Io<IO>::elem;
     const E* x = static_cast<const E*>(a.x);
     const E* Bm = static_cast<const E*>(a.B);
     const int col = lane & 15, grp = lane >> 4;
-    const int dl = d0 + 4 * col;  // this lane's channels dl..dl+3 (all inside or all outside: Di % 16 == 0)
-    const bool dok = dl < a.Di;
+    // This lane's channels dl..dl+3. A lane past d_inner (Di % 16 == 0: all four or none) reads
+    // the last four channels instead: its MFMA column feeds only outputs of its own (invalid)
+    // channels, which are never stored. Every load below is unconditional and in bounds, so the
+    // loads of a group are all in flight together; a token past the range is read at the range's
+    // last token and its x and B' are zeroed by a select, which keeps it out of the sums even when
+    // that token holds NaN or Inf.
+    const int dl = min(d0 + 4 * col, a.Di - 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[q][nb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int t0 = tb + wave * kTile; t0 < te; t0 += kWaves * kTile) {
-        if constexpr (sizeof(E) == 2) {
-            // K = 16 tokens: the lane supplies tokens t0 + 4 grp + e, e = 0..3
-            uint2 xr[4];
-            float mv[4];
+    for (int g0 = tb + wave * kTile; g0 < te; g0 += G * kWaves * kTile) {
+        // the lane's token of slot (gi, e): bf16 t0 + 4 grp + e (K = 16), fp32 t0 + 4 e + grp
+        // (four K = 4 steps), t0 = g0 + 64 gi
+        auto token = [&](int gi, int e) {
+            return g0 + gi * kWaves * kTile + (sizeof(E) == 2 ? 4 * grp + e : 4 * e + grp);
+        };
+        using XRaw = typename std::conditional<sizeof(E) == 2, uint2, float4>::type;
+        XRaw xr[G][4];
+        float mv[G][4];
+        E braw[G][NB][4];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int tok = t0 + 4 * grp + e;
-                const bool ok = tok < te;
-                xr[e] = (ok && dok) ? *reinterpret_cast<const uint2*>(x + (row0 + tok) * a.Di + dl) : make_uint2(0u, 0u);
-                mv[e] = ok ? a.m[row0 + tok] : 0.0f;
-            }
-            v4s bx[4];
+                const int64_t row = row0 + min(token(gi, e), te - 1);
+                xr[gi][e] = *reinterpret_cast<const XRaw*>(x + row * a.Di + dl);
+                mv[gi][e] = a.m[row];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bx[0][e] = static_cast<short>(xr[e].x & 0xffffu);
-                bx[1][e] = static_cast<short>(xr[e].x >> 16);
-                bx[2][e] = static_cast<short>(xr[e].y & 0xffffu);
-                bx[3][e] = static_cast<short>(xr[e].y >> 16);
+                for (int nb = 0; nb < NB; ++nb) braw[gi][nb][e] = Bm[row * N + nb * 16 + col];
             }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                v4s ah, al;
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (token(gi, e) >= te) {   // a select: both values are already loaded
+                    xr[gi][e] = XRaw{};
+                    mv[gi][e] = 0.0f;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) braw[gi][nb][e] = E{};
+                }
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            if constexpr (sizeof(E) == 2) {
+                v4s bx[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int tok = t0 + 4 * grp + e;
-                    const float bv = tok < te ? ld_val(Bm, (row0 + tok) * N + nb * 16 + col) * mv[e] : 0.0f;
-                    const HiLo hl = split_bf16(bv);
-                    ah[e] = hl.hi;
-                    al[e] = hl.lo;
+                    bx[0][e] = static_cast<short>(xr[gi][e].x & 0xffffu);
+                    bx[1][e] = static_cast<short>(xr[gi][e].x >> 16);
+                    bx[2][e] = static_cast<short>(xr[gi][e].y & 0xffffu);
+                    bx[3][e] = static_cast<short>(xr[gi][e].y >> 16);
                 }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[q][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bx[q], acc[q][nb], 0, 0, 0);
-                    acc[q][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bx[q], acc[q][nb], 0, 0, 0);
-                }
-            }
-        } else {
-            // four K = 4 steps: step k's lane supplies token t0 + 4 k + grp
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int tok = t0 + 4 * k + grp;
-                const bool ok = tok < te;
-                const float4 xv = (ok && dok) ? *reinterpret_cast<const float4*>(x + (row0 + tok) * a.Di + dl)
-                                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                const float mv = ok ? a.m[row0 + tok] : 0.0f;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const float bv = ok ? ld_val(Bm, (row0 + tok) * N + nb * 16 + col) * mv : 0.0f;
-                    acc[0][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.x, acc[0][nb], 0, 0, 0);
-                    acc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.y, acc[1][nb], 0, 0, 0);
-                    acc[2][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.z, acc[2][nb], 0, 0, 0);
-                    acc[3][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xv.w, acc[3][nb], 0, 0, 0);
+                    v4s ah, al;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const HiLo hl = split_bf16(from_bf16(braw[gi][nb][e]) * mv[gi][e]);
+                        ah[e] = hl.hi;
+                        al[e] = hl.lo;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[q][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bx[q], acc[q][nb], 0, 0, 0);
+                        acc[q][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bx[q], acc[q][nb], 0, 0, 0);
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const float bv = braw[gi][nb][e] * mv[gi][e];
+                        acc[0][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xr[gi][e].x, acc[0][nb], 0, 0, 0);
+                        acc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xr[gi][e].y, acc[1][nb], 0, 0, 0);
+                        acc[2][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xr[gi][e].z, acc[2][nb], 0, 0, 0);
+                        acc[3][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv, xr[gi][e].w, acc[3][nb], 0, 0, 0);
+                    }
             }
         }
     }
@@ -179,23 +216,57 @@ __device__ __forceinline__ void park_state(float4 (*red)[16 * NB][kBlock / 4], i
             red[wave][nb * 16 + 4 * grp + r][col] = make_float4(acc[0][nb][r], acc[1][nb][r], acc[2][nb][r], acc[3][nb][r]);
 }
 
-// The readout of one wave: y = C H for the 16-token tiles i0 = gb + 16 wave, gb + 16 (wave + 4),
-// ... below ge and the 64 channels d0..d0+63. hval(n, c) returns the state at n for channel
-// d0 + c. MFMA q's row r is channel d0 + 16 (r / 4) + 4 q + (r % 4): as the A operand this
-// lane supplies row col; as the output it holds rows 4 grp + 0..3, i.e. 16 consecutive channels
-// d0 + 16 grp + 0..15 of token i0 + col.
-template <typename IO, int NB, typename HVal>
-__device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0, int gb, int ge, int wave, int lane,
-                                          HVal hval) {
+// C rows of the readout, kOutGroup<NB> tiles at a time, as the B operands of this lane: bf16, the
+// four states 16 nb + 4 grp + 0..3 of token t0 + col (t0 = g0 + 64 gi) packed in a uint2; fp32,
+// state 16 nb + 4 k + grp of that token for the four K = 4 steps k. The readout's first group is
+// loaded before the state contraction, so its latency is hidden behind that pass.
+template <int NB> constexpr int kOutGroup = NB >= 4 ? 2 : 4;
+template <typename IO, int NB> struct CRows;
+template <int NB> struct CRows<uint16_t, NB> { uint2 v[kOutGroup<NB>][NB]; };
+template <int NB> struct CRows<float, NB> { float v[kOutGroup<NB>][NB][4]; };
+
+template <typename IO, int NB>
+__device__ __forceinline__ void load_c(const NcArgs& a, int64_t row0, int g0, int ge, int lane, CRows<IO, NB>& c) {
     constexpr int N = 16 * NB;
     using E = typename Io<IO>::elem;
     const E* Cm = static_cast<const E*>(a.C);
+    const int col = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int gi = 0; gi < kOutGroup<NB>; ++gi) {
+        // a token past the group reads the group's last row (only its own output column, never
+        // stored, depends on it): the loads are unconditional and in bounds
+        const int64_t row = row0 + min(g0 + gi * kWaves * kTile + col, ge - 1);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if constexpr (sizeof(E) == 2) {
+                c.v[gi][nb] = *reinterpret_cast<const uint2*>(Cm + row * N + nb * 16 + 4 * grp);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) c.v[gi][nb][k] = Cm[row * N + nb * 16 + 4 * k + grp];
+            }
+        }
+    }
+}
+
+// The readout of one wave: y = C H for the 16-token tiles i0 = gb + 16 wave, gb + 16 (wave + 4),
+// ... below ge and the 64 channels d0..d0+63. hval(n, c) returns the state at n for channel
+// d0 + c; cr holds the C rows of the wave's first group of tiles. MFMA q's row r is channel
+// d0 + 16 (r / 4) + 4 q + (r % 4): as the A operand this lane supplies row col; as the output
+// it holds rows 4 grp + 0..3, i.e. 16 consecutive channels d0 + 16 grp + 0..15 of token
+// i0 + col; the tile is regrouped into whole rows through the wave's LDS area stage before it
+// is stored.
+template <typename IO, int NB, typename HVal>
+__device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0, int gb, int ge, int wave, int lane,
+                                          HVal hval, uint32_t* stage, CRows<IO, NB> cr) {
+    constexpr int G = kOutGroup<NB>;
+    using E = typename Io<IO>::elem;
     E* y = static_cast<E*>(a.y);
     const int col = lane & 15, grp = lane >> 4;
-    const int arow = 16 * (col >> 2) + (col & 3);  // channel of A row col in MFMA 0, less d0
-    const bool aok = d0 + 16 * (col >> 2) < a.Di;
-    const int dout = d0 + 16 * grp;
-    const bool ook = dout < a.Di;
+    // A row col's channel in MFMA q is d0 + arow + 4 q; a row past d_inner reads channel
+    // d_inner - 1 instead (only its own output row, never stored, depends on it).
+    const int arow = 16 * (col >> 2) + (col & 3);
+    const int amax = a.Di - 1 - d0;
+    const int first = gb + wave * kTile;
 
     if constexpr (sizeof(E) == 2) {
         v4s ah[4][NB], al[4][NB];
@@ -205,42 +276,52 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float h = aok ? hval(nb * 16 + 4 * grp + e, arow + 4 * q) : 0.0f;
+                    const float h = hval(nb * 16 + 4 * grp + e, min(arow + 4 * q, amax));
                     const HiLo hl = split_bf16(h);
                     ah[q][nb][e] = hl.hi;
                     al[q][nb][e] = hl.lo;
                 }
-        for (int i0 = gb + wave * kTile; i0 < ge; i0 += kWaves * kTile) {
-            const int tok = i0 + col;  // this lane's token as the B operand and in the output
-            const bool tok_ok = tok < ge;
-            v4f acc[4];
+        for (int g0 = first; g0 < ge; g0 += G * kWaves * kTile) {
+            if (g0 != first) load_c<IO, NB>(a, row0, g0, ge, lane, cr);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int gi = 0; gi < G; ++gi) {
+                if (g0 + gi * kWaves * kTile >= ge) break;
+                v4f acc[4];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const uint2 cr = tok_ok ? *reinterpret_cast<const uint2*>(Cm + (row0 + tok) * N + nb * 16 + 4 * grp)
-                                        : make_uint2(0u, 0u);
-                v4s bc;
-                bc[0] = static_cast<short>(cr.x & 0xffffu);
-                bc[1] = static_cast<short>(cr.x >> 16);
-                bc[2] = static_cast<short>(cr.y & 0xffffu);
-                bc[3] = static_cast<short>(cr.y >> 16);
+                for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah[q][nb], bc, acc[q], 0, 0, 0);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al[q][nb], bc, acc[q], 0, 0, 0);
+                for (int nb = 0; nb < NB; ++nb) {
+                    v4s bc;
+                    bc[0] = static_cast<short>(cr.v[gi][nb].x & 0xffffu);
+                    bc[1] = static_cast<short>(cr.v[gi][nb].x >> 16);
+                    bc[2] = static_cast<short>(cr.v[gi][nb].y & 0xffffu);
+                    bc[3] = static_cast<short>(cr.v[gi][nb].y >> 16);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah[q][nb], bc, acc[q], 0, 0, 0);
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al[q][nb], bc, acc[q], 0, 0, 0);
+                    }
                 }
-            }
-            if (tok_ok && ook) {
                 uint32_t w[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     w[2 * q] = static_cast<uint32_t>(to_bf16(acc[q][0])) | (static_cast<uint32_t>(to_bf16(acc[q][1])) << 16);
-                    w[2 * q + 1] = static_cast<uint32_t>(to_bf16(acc[q][2])) | (static_cast<uint32_t>(to_bf16(acc[q][3])) << 16);
+                    w[2 * q + 1] =
+                        static_cast<uint32_t>(to_bf16(acc[q][2])) | (static_cast<uint32_t>(to_bf16(acc[q][3])) << 16);
                 }
-                uint4* dst = reinterpret_cast<uint4*>(y + (row0 + tok) * a.Di + dout);
-                dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-                dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+                // through the wave's LDS tile [16 tokens][64 channels] (rows padded to 36 words) so
+                // that each store instruction writes eight whole 128-byte rows
+                uint4* srow = reinterpret_cast<uint4*>(stage + col * kStageRow + 8 * grp);
+                srow[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                srow[1] = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 8 * h + (lane >> 3), c8 = lane & 7;  // row of the tile, 8-channel piece
+                    const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kStageRow + 4 * c8);
+                    const int t = g0 + gi * kWaves * kTile + r;
+                    if (t < ge && d0 + 8 * c8 < a.Di)
+                        *reinterpret_cast<uint4*>(y + (row0 + t) * a.Di + d0 + 8 * c8) = v;
+                }
             }
         }
     } else {
@@ -251,26 +332,35 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) ha[q][nb][k] = aok ? hval(nb * 16 + 4 * k + grp, arow + 4 * q) : 0.0f;
-        for (int i0 = gb + wave * kTile; i0 < ge; i0 += kWaves * kTile) {
-            const int tok = i0 + col;
-            const bool tok_ok = tok < ge;
-            v4f acc[4];
+                for (int k = 0; k < 4; ++k) ha[q][nb][k] = hval(nb * 16 + 4 * k + grp, min(arow + 4 * q, amax));
+        for (int g0 = first; g0 < ge; g0 += G * kWaves * kTile) {
+            if (g0 != first) load_c<IO, NB>(a, row0, g0, ge, lane, cr);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int gi = 0; gi < G; ++gi) {
+                if (g0 + gi * kWaves * kTile >= ge) break;
+                v4f acc[4];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+                for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float cv = tok_ok ? Cm[(row0 + tok) * N + nb * 16 + 4 * k + grp] : 0.0f;
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[q][nb][k], cv, acc[q], 0, 0, 0);
+                    for (int k = 0; k < 4; ++k)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[q][nb][k], cr.v[gi][nb][k], acc[q], 0, 0, 0);
+                // through the wave's LDS tile [16 tokens][64 channels] (rows padded to 68 words):
+                // each store instruction writes four whole 256-byte rows
+                float4* srow = reinterpret_cast<float4*>(stage + col * kStageRowF + 16 * grp);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) srow[q] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const int r = 4 * h + (lane >> 4), c4 = lane & 15;  // row of the tile, 4-channel piece
+                    const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageRowF + 4 * c4);
+                    const int t = g0 + gi * kWaves * kTile + r;
+                    if (t < ge && d0 + 4 * c4 < a.Di)
+                        *reinterpret_cast<float4*>(y + (row0 + t) * a.Di + d0 + 4 * c4) = v;
                 }
-            if (tok_ok && ook) {
-                float4* dst = reinterpret_cast<float4*>(y + (row0 + tok) * a.Di + dout);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) dst[q] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
             }
         }
     }
@@ -285,21 +375,28 @@ template <typename IO, int NB>
 __global__ __launch_bounds__(256) void k_ncssd_fused(NcArgs a) {
     constexpr int N = 16 * NB;
     __shared__ float4 red[kWaves][N][kBlock / 4];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][kStageWords<IO>];
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = static_cast<int>(threadIdx.x) >> 6;
-    const int d0 = static_cast<int>(blockIdx.x % a.ncb) * kBlock;
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x / a.ncb) * a.T;
+    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int d0 = (lid % a.ncb) * kBlock;
+    const int64_t row0 = static_cast<int64_t>(lid / a.ncb) * a.T;
+    CRows<IO, NB> cr;
+    load_c<IO, NB>(a, row0, wave * kTile, a.T, lane, cr);  // in flight during the state pass
     v4f acc[4][NB];
     state_tiles<IO, NB>(a, row0, d0, 0, a.T, wave, lane, acc);
     park_state<NB>(red, wave, lane, acc);
     __syncthreads();
     const float* rf = reinterpret_cast<const float*>(&red[0][0][0]);
-    out_tiles<IO, NB>(a, row0, d0, 0, a.T, wave, lane, [&](int n, int c) {
-        float v = 0.0f;
+    out_tiles<IO, NB>(
+        a, row0, d0, 0, a.T, wave, lane,
+        [&](int n, int c) {
+            float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += rf[(w * N + n) * kBlock + c];  // waves in a fixed order
-        return v;
-    });
+            for (int w = 0; w < kWaves; ++w) v += rf[(w * N + n) * kBlock + c];  // waves in a fixed order
+            return v;
+        },
+        stage[wave], cr);
 }
 
 // Pass 1 of a split sequence: the partial state of one token range. One workgroup per (channel
@@ -310,9 +407,10 @@ __global__ __launch_bounds__(256) void k_ncssd_state(NcArgs a) {
     __shared__ float4 red[kWaves][N][kBlock / 4];
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = static_cast<int>(threadIdx.x) >> 6;
-    const int d0 = static_cast<int>(blockIdx.x % a.ncb) * kBlock;
-    const int split = static_cast<int>((blockIdx.x / a.ncb) % a.splits);
-    const int s = static_cast<int>(blockIdx.x / a.ncb / a.splits);
+    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int d0 = (lid % a.ncb) * kBlock;
+    const int split = (lid / a.ncb) % a.splits;
+    const int s = lid / a.ncb / a.splits;
     const int tb = split * a.span;
     const int te = min(tb + a.span, a.T);
     v4f acc[4][NB];
@@ -360,14 +458,19 @@ template <typename IO, int NB>
 __global__ __launch_bounds__(256) void k_ncssd_out(NcArgs a) {
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = static_cast<int>(threadIdx.x) >> 6;
-    const int d0 = static_cast<int>(blockIdx.x % a.ncb) * kBlock;
-    const int gb = static_cast<int>((blockIdx.x / a.ncb) % a.groups) * kOutTokens;
-    const int s = static_cast<int>(blockIdx.x / a.ncb / a.groups);
+    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int d0 = (lid % a.ncb) * kBlock;
+    const int gb = ((lid / a.ncb) % a.groups) * kOutTokens;
+    const int s = lid / a.ncb / a.groups;
     const int ge = min(gb + kOutTokens, a.T);
     const float* Hs = a.H + static_cast<int64_t>(s) * 16 * NB * a.Di + d0;
     const int Di = a.Di;
-    out_tiles<IO, NB>(a, static_cast<int64_t>(s) * a.T, d0, gb, ge, wave, lane,
-                      [&](int n, int c) { return Hs[static_cast<int64_t>(n) * Di + c]; });
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][kStageWords<IO>];
+    CRows<IO, NB> cr;
+    load_c<IO, NB>(a, static_cast<int64_t>(s) * a.T, gb + wave * kTile, ge, lane, cr);
+    out_tiles<IO, NB>(
+        a, static_cast<int64_t>(s) * a.T, d0, gb, ge, wave, lane,
+        [&](int n, int c) { return Hs[static_cast<int64_t>(n) * Di + c]; }, stage[wave], cr);
 }
 
 // ---------------------------------------------------------------------------------------------
