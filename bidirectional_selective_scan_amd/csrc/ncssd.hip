@@ -11,7 +11,7 @@
 // Execution design (gfx950, wave64, MFMA 16x16 tiles):
 //  * A workgroup owns one sequence and 64 channels (k_ncssd_fused): its four waves take the
 //    sequence's 16-token tiles round-robin for the state, add their partial states through LDS
-//    in a fixed order, and read the state out for the same tiles: x is read once, y written
+//    in wave order, and read the state out for the same tiles: x is read once, y written
 //    once, H never leaves the chip. Long sequences with too few workgroups for the chip are
 //    split instead: pass 1 (k_ncssd_state) stores one partial state per token range, a small
 //    kernel (k_ncssd_reduce) adds them in range order into H in the workspace, and pass 2
@@ -22,10 +22,13 @@
 //    plain 8-byte (bf16) or 16-byte (fp32) row loads, so X needs no transposition through LDS:
 //    the four MFMA column sets of a wave are the channels d0 + 4c + q, q = 0..3, and the lane
 //    regroups its loads into one operand per q.
-//  * The readout computes Y^T = H^T C^T: rows = channels, K = states, columns = 16
-//    tokens. The channel of MFMA q's row r is d0 + 16 (r / 4) + 4 q + (r % 4), so the four
-//    accumulators a lane ends with hold 16 consecutive channels of one token: y leaves as 16-byte
-//    stores. The H operand is loaded once per wave; per tile only the C rows are read.
+//  * The readout computes Y^T = H^T C^T: rows = channels, K = states, columns = 16 tokens.
+//    MFMA q's row m is channel d0 + 4 m + q, the column mapping of the state contraction, so a
+//    lane's state accumulators are already its A operand (the four waves' partial states are
+//    added lane by lane through LDS), and the four accumulators a lane ends with hold 16
+//    consecutive channels of one token; a per-wave LDS tile regroups them so every store
+//    instruction writes whole rows. The C rows of a wave's first readout tiles are loaded
+//    before the state pass.
 //  * bf16 io: X and C are exact bf16 MFMA operands. B . m and H are fp32 values; each is split
 //    into a bf16 high part and a bf16 remainder and both are multiplied (two MFMAs), so the
 //    contraction keeps about 16 significant bits on those operands and accumulates in fp32.
@@ -204,31 +207,49 @@ __device__ __forceinline__ void state_tiles(const NcArgs& a, int64_t row0, int d
     }
 }
 
-// Every wave's state contraction into LDS: red[wave][n][c] holds channels d0 + 4c + 0..3.
+// The four waves' partial states added in wave order through LDS: every wave ends with the
+// workgroup's state in its own accumulator layout, h[q][nb][r] = state n = 16 nb + 4 grp + r of
+// channel d0 + 4 col + q. red holds one float4 per (wave, q, nb, lane).
 template <int NB>
-__device__ __forceinline__ void park_state(float4 (*red)[16 * NB][kBlock / 4], int wave, int lane,
-                                           const v4f (&acc)[4][NB]) {
-    const int col = lane & 15, grp = lane >> 4;
+__device__ __forceinline__ void sum_waves(float4 (*red)[4 * NB][64], int wave, int lane, const v4f (&acc)[4][NB],
+                                          v4f (&h)[4][NB]) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            red[wave][nb * 16 + 4 * grp + r][col] = make_float4(acc[0][nb][r], acc[1][nb][r], acc[2][nb][r], acc[3][nb][r]);
+        for (int nb = 0; nb < NB; ++nb)
+            red[wave][q * NB + nb][lane] = make_float4(acc[q][nb][0], acc[q][nb][1], acc[q][nb][2], acc[q][nb][3]);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float4 v = red[0][q * NB + nb][lane];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) {
+                const float4 o = red[w][q * NB + nb][lane];
+                v.x += o.x;
+                v.y += o.y;
+                v.z += o.z;
+                v.w += o.w;
+            }
+            h[q][nb] = v4f{v.x, v.y, v.z, v.w};
+        }
 }
 
-// C rows of the readout, kOutGroup<NB> tiles at a time, as the B operands of this lane: bf16, the
-// four states 16 nb + 4 grp + 0..3 of token t0 + col (t0 = g0 + 64 gi) packed in a uint2; fp32,
-// state 16 nb + 4 k + grp of that token for the four K = 4 steps k. The readout's first group is
-// loaded before the state contraction, so its latency is hidden behind that pass.
+// C rows of the readout, kOutGroup<NB> tiles at a time, as the B operands of this lane: the four
+// states 16 nb + 4 grp + 0..3 of token t0 + col (t0 = g0 + 64 gi), bf16 packed in a uint2 or
+// fp32 in a float4. The readout's first group is loaded before the state contraction, so its
+// latency is hidden behind that pass.
 template <int NB> constexpr int kOutGroup = NB >= 4 ? 2 : 4;
 template <typename IO, int NB> struct CRows;
 template <int NB> struct CRows<uint16_t, NB> { uint2 v[kOutGroup<NB>][NB]; };
-template <int NB> struct CRows<float, NB> { float v[kOutGroup<NB>][NB][4]; };
+template <int NB> struct CRows<float, NB> { float4 v[kOutGroup<NB>][NB]; };
 
 template <typename IO, int NB>
 __device__ __forceinline__ void load_c(const NcArgs& a, int64_t row0, int g0, int ge, int lane, CRows<IO, NB>& c) {
     constexpr int N = 16 * NB;
     using E = typename Io<IO>::elem;
+    using V = typename std::conditional<sizeof(E) == 2, uint2, float4>::type;
     const E* Cm = static_cast<const E*>(a.C);
     const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -237,35 +258,26 @@ __device__ __forceinline__ void load_c(const NcArgs& a, int64_t row0, int g0, in
         // stored, depends on it): the loads are unconditional and in bounds
         const int64_t row = row0 + min(g0 + gi * kWaves * kTile + col, ge - 1);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            if constexpr (sizeof(E) == 2) {
-                c.v[gi][nb] = *reinterpret_cast<const uint2*>(Cm + row * N + nb * 16 + 4 * grp);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) c.v[gi][nb][k] = Cm[row * N + nb * 16 + 4 * k + grp];
-            }
-        }
+        for (int nb = 0; nb < NB; ++nb) c.v[gi][nb] = *reinterpret_cast<const V*>(Cm + row * N + nb * 16 + 4 * grp);
     }
 }
 
 // The readout of one wave: y = C H for the 16-token tiles i0 = gb + 16 wave, gb + 16 (wave + 4),
-// ... below ge and the 64 channels d0..d0+63. hval(n, c) returns the state at n for channel
-// d0 + c; cr holds the C rows of the wave's first group of tiles. MFMA q's row r is channel
-// d0 + 16 (r / 4) + 4 q + (r % 4): as the A operand this lane supplies row col; as the output
-// it holds rows 4 grp + 0..3, i.e. 16 consecutive channels d0 + 16 grp + 0..15 of token
-// i0 + col; the tile is regrouped into whole rows through the wave's LDS area stage before it
-// is stored.
-template <typename IO, int NB, typename HVal>
+// ... below ge and the 64 channels d0..d0+63. MFMA q's row m is channel d0 + 4 m + q, the
+// column mapping of the state contraction, so h (in that pass's accumulator layout) is already
+// this lane's A operand: row col, states 16 nb + 4 grp + e. The K index e of a 16x16x16 bf16
+// step, or the step s of the four 16x16x4 fp32 steps, is state 16 nb + 4 grp + e (or + s), and
+// the C operand follows the same order. The output lane holds rows 4 grp + r, i.e. channels
+// d0 + 16 grp + 4 r + q of token i0 + col: 16 consecutive channels, regrouped into whole rows
+// through the wave's LDS area stage before they are stored. cr holds the C rows of the wave's
+// first group of tiles.
+template <typename IO, int NB>
 __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0, int gb, int ge, int wave, int lane,
-                                          HVal hval, uint32_t* stage, CRows<IO, NB> cr) {
+                                          const v4f (&h)[4][NB], uint32_t* stage, CRows<IO, NB> cr) {
     constexpr int G = kOutGroup<NB>;
     using E = typename Io<IO>::elem;
     E* y = static_cast<E*>(a.y);
     const int col = lane & 15, grp = lane >> 4;
-    // A row col's channel in MFMA q is d0 + arow + 4 q; a row past d_inner reads channel
-    // d_inner - 1 instead (only its own output row, never stored, depends on it).
-    const int arow = 16 * (col >> 2) + (col & 3);
-    const int amax = a.Di - 1 - d0;
     const int first = gb + wave * kTile;
 
     if constexpr (sizeof(E) == 2) {
@@ -276,8 +288,7 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float h = hval(nb * 16 + 4 * grp + e, min(arow + 4 * q, amax));
-                    const HiLo hl = split_bf16(h);
+                    const HiLo hl = split_bf16(h[q][nb][e]);
                     ah[q][nb][e] = hl.hi;
                     al[q][nb][e] = hl.lo;
                 }
@@ -302,12 +313,13 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
                         acc[q] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al[q][nb], bc, acc[q], 0, 0, 0);
                     }
                 }
+                // channel 16 grp + 4 r + q is acc[q][r]; pairs (q = 0, 1) and (2, 3) share a word
                 uint32_t w[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    w[2 * q] = static_cast<uint32_t>(to_bf16(acc[q][0])) | (static_cast<uint32_t>(to_bf16(acc[q][1])) << 16);
-                    w[2 * q + 1] =
-                        static_cast<uint32_t>(to_bf16(acc[q][2])) | (static_cast<uint32_t>(to_bf16(acc[q][3])) << 16);
+                for (int r = 0; r < 4; ++r) {
+                    w[2 * r] = static_cast<uint32_t>(to_bf16(acc[0][r])) | (static_cast<uint32_t>(to_bf16(acc[1][r])) << 16);
+                    w[2 * r + 1] =
+                        static_cast<uint32_t>(to_bf16(acc[2][r])) | (static_cast<uint32_t>(to_bf16(acc[3][r])) << 16);
                 }
                 // through the wave's LDS tile [16 tokens][64 channels] (rows padded to 36 words) so
                 // that each store instruction writes eight whole 128-byte rows
@@ -315,8 +327,8 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
                 srow[0] = make_uint4(w[0], w[1], w[2], w[3]);
                 srow[1] = make_uint4(w[4], w[5], w[6], w[7]);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int r = 8 * h + (lane >> 3), c8 = lane & 7;  // row of the tile, 8-channel piece
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = 8 * hh + (lane >> 3), c8 = lane & 7;  // row of the tile, 8-channel piece
                     const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kStageRow + 4 * c8);
                     const int t = g0 + gi * kWaves * kTile + r;
                     if (t < ge && d0 + 8 * c8 < a.Di)
@@ -325,14 +337,6 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
             }
         }
     } else {
-        // K = 4 steps: step k's lane supplies state n = 16 nb + 4 k + grp
-        float ha[4][NB][4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) ha[q][nb][k] = hval(nb * 16 + 4 * k + grp, min(arow + 4 * q, amax));
         for (int g0 = first; g0 < ge; g0 += G * kWaves * kTile) {
             if (g0 != first) load_c<IO, NB>(a, row0, g0, ge, lane, cr);
 #pragma unroll
@@ -342,20 +346,22 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
 #pragma unroll
                 for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float cs[4] = {cr.v[gi][nb].x, cr.v[gi][nb].y, cr.v[gi][nb].z, cr.v[gi][nb].w};
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
+                    for (int st = 0; st < 4; ++st)
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[q][nb][k], cr.v[gi][nb][k], acc[q], 0, 0, 0);
+                            acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(h[q][nb][st], cs[st], acc[q], 0, 0, 0);
+                }
                 // through the wave's LDS tile [16 tokens][64 channels] (rows padded to 68 words):
                 // each store instruction writes four whole 256-byte rows
                 float4* srow = reinterpret_cast<float4*>(stage + col * kStageRowF + 16 * grp);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) srow[q] = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+                for (int r = 0; r < 4; ++r) srow[r] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const int r = 4 * h + (lane >> 4), c4 = lane & 15;  // row of the tile, 4-channel piece
+                for (int hh = 0; hh < 4; ++hh) {
+                    const int r = 4 * hh + (lane >> 4), c4 = lane & 15;  // row of the tile, 4-channel piece
                     const float4 v = *reinterpret_cast<const float4*>(stage + r * kStageRowF + 4 * c4);
                     const int t = g0 + gi * kWaves * kTile + r;
                     if (t < ge && d0 + 4 * c4 < a.Di)
@@ -373,8 +379,7 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
 
 template <typename IO, int NB>
 __global__ __launch_bounds__(256) void k_ncssd_fused(NcArgs a) {
-    constexpr int N = 16 * NB;
-    __shared__ float4 red[kWaves][N][kBlock / 4];
+    __shared__ float4 red[kWaves][4 * NB][64];
     __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][kStageWords<IO>];
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = static_cast<int>(threadIdx.x) >> 6;
@@ -383,20 +388,10 @@ __global__ __launch_bounds__(256) void k_ncssd_fused(NcArgs a) {
     const int64_t row0 = static_cast<int64_t>(lid / a.ncb) * a.T;
     CRows<IO, NB> cr;
     load_c<IO, NB>(a, row0, wave * kTile, a.T, lane, cr);  // in flight during the state pass
-    v4f acc[4][NB];
+    v4f acc[4][NB], h[4][NB];
     state_tiles<IO, NB>(a, row0, d0, 0, a.T, wave, lane, acc);
-    park_state<NB>(red, wave, lane, acc);
-    __syncthreads();
-    const float* rf = reinterpret_cast<const float*>(&red[0][0][0]);
-    out_tiles<IO, NB>(
-        a, row0, d0, 0, a.T, wave, lane,
-        [&](int n, int c) {
-            float v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) v += rf[(w * N + n) * kBlock + c];  // waves in a fixed order
-            return v;
-        },
-        stage[wave], cr);
+    sum_waves<NB>(red, wave, lane, acc, h);
+    out_tiles<IO, NB>(a, row0, d0, 0, a.T, wave, lane, h, stage[wave], cr);
 }
 
 // Pass 1 of a split sequence: the partial state of one token range. One workgroup per (channel
@@ -404,34 +399,28 @@ __global__ __launch_bounds__(256) void k_ncssd_fused(NcArgs a) {
 template <typename IO, int NB>
 __global__ __launch_bounds__(256) void k_ncssd_state(NcArgs a) {
     constexpr int N = 16 * NB;
-    __shared__ float4 red[kWaves][N][kBlock / 4];
+    __shared__ float4 red[kWaves][4 * NB][64];
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int col = lane & 15, grp = lane >> 4;
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int d0 = (lid % a.ncb) * kBlock;
     const int split = (lid / a.ncb) % a.splits;
     const int s = lid / a.ncb / a.splits;
     const int tb = split * a.span;
     const int te = min(tb + a.span, a.T);
-    v4f acc[4][NB];
+    v4f acc[4][NB], h[4][NB];
     state_tiles<IO, NB>(a, static_cast<int64_t>(s) * a.T, d0, tb, te, wave, lane, acc);
-    park_state<NB>(red, wave, lane, acc);
-    __syncthreads();
-    // 256 threads add the four waves' blocks (N x 16 float4) and store them
-    float* dst = a.part + (static_cast<int64_t>(s) * a.splits + split) * N * a.Di + d0;
-    for (int i = static_cast<int>(threadIdx.x); i < N * (kBlock / 4); i += kBlock * kWaves) {
-        const int n = i / (kBlock / 4), c = i % (kBlock / 4);
-        if (d0 + 4 * c >= a.Di) continue;
-        float4 v = red[0][n][c];
+    sum_waves<NB>(red, wave, lane, acc, h);
+    // wave 0 stores the block: state n = 16 nb + 4 grp + r, channels d0 + 4 col + 0..3
+    if (wave == 0 && d0 + 4 * col < a.Di) {
+        float* dst = a.part + (static_cast<int64_t>(s) * a.splits + split) * N * a.Di + d0 + 4 * col;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) {
-            const float4 o = red[w][n][c];
-            v.x += o.x;
-            v.y += o.y;
-            v.z += o.z;
-            v.w += o.w;
-        }
-        *reinterpret_cast<float4*>(dst + static_cast<int64_t>(n) * a.Di + 4 * c) = v;
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<float4*>(dst + static_cast<int64_t>(nb * 16 + 4 * grp + r) * a.Di) =
+                    make_float4(h[0][nb][r], h[1][nb][r], h[2][nb][r], h[3][nb][r]);
     }
 }
 
@@ -456,21 +445,34 @@ __global__ __launch_bounds__(256) void k_ncssd_reduce(NcArgs a, int64_t quads, i
 // workgroup per (channel block, token group, sequence), in that order of speed.
 template <typename IO, int NB>
 __global__ __launch_bounds__(256) void k_ncssd_out(NcArgs a) {
+    constexpr int N = 16 * NB;
+    __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][kStageWords<IO>];
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = static_cast<int>(threadIdx.x) >> 6;
+    const int col = lane & 15, grp = lane >> 4;
     const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int d0 = (lid % a.ncb) * kBlock;
     const int gb = ((lid / a.ncb) % a.groups) * kOutTokens;
     const int s = lid / a.ncb / a.groups;
     const int ge = min(gb + kOutTokens, a.T);
-    const float* Hs = a.H + static_cast<int64_t>(s) * 16 * NB * a.Di + d0;
-    const int Di = a.Di;
-    __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][kStageWords<IO>];
+    const int64_t row0 = static_cast<int64_t>(s) * a.T;
     CRows<IO, NB> cr;
-    load_c<IO, NB>(a, static_cast<int64_t>(s) * a.T, gb + wave * kTile, ge, lane, cr);
-    out_tiles<IO, NB>(
-        a, static_cast<int64_t>(s) * a.T, d0, gb, ge, wave, lane,
-        [&](int n, int c) { return Hs[static_cast<int64_t>(n) * Di + c]; }, stage[wave], cr);
+    load_c<IO, NB>(a, row0, gb + wave * kTile, ge, lane, cr);
+    // this lane's state values in the accumulator layout; a lane past d_inner reads the last four
+    // channels (only its own output rows, never stored, depend on them)
+    const float* Hs = a.H + static_cast<int64_t>(s) * N * a.Di + min(d0 + 4 * col, a.Di - 4);
+    v4f h[4][NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 v = *reinterpret_cast<const float4*>(Hs + static_cast<int64_t>(nb * 16 + 4 * grp + r) * a.Di);
+            h[0][nb][r] = v.x;
+            h[1][nb][r] = v.y;
+            h[2][nb][r] = v.z;
+            h[3][nb][r] = v.w;
+        }
+    out_tiles<IO, NB>(a, row0, d0, gb, ge, wave, lane, h, stage[wave], cr);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -590,7 +592,7 @@ int vimscan_ncssd_fwd(const void* x, const void* B, const void* C, const float* 
     if (!x || !B || !C || !m || !y) return VIMSCAN_ERR_NULL;
     const bool bf = launch->io_dtype == VIMSCAN_BF16;
     const size_t e = bf ? 2 : 4;
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(B, e) || !aligned(C, bf ? 8 : 4) || !aligned(m, 4))
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(B, e) || !aligned(C, bf ? 8 : 16) || !aligned(m, 4))
         return VIMSCAN_ERR_ALIGN;
     const size_t tokens = static_cast<size_t>(launch->batch) * launch->seqlen;
     const size_t ny = tokens * launch->d_inner * e;

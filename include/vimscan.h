@@ -202,7 +202,7 @@ int vimscan_fwd(const void* x, const void* dt, const void* z, const void* B, con
  * sets the tokens of a sequence that one workgroup of the state pass sums (rounded up to a
  * multiple of 16; 0: the library picks); scan_events, when set, are recorded before the first
  * and after the last kernel. x and y must be 16-byte aligned, B aligned to its element size, C to
- * 8 bytes (bf16) or 4 (fp32), m to 4 (VIMSCAN_ERR_ALIGN). When one workgroup covers a whole
+ * 8 bytes (bf16) or 16 (fp32), m to 4 (VIMSCAN_ERR_ALIGN). When one workgroup covers a whole
  * sequence, H stays on the chip and no workspace is needed; when long sequences are split
  * (vimscan_ncssd_plan: chunks > 1) the workspace holds the split partial states and H. fp32 io runs the fp32 matrix-core contraction; bf16 io multiplies the
  * exact bf16 x and C by B*m and H each split into two bf16 parts, accumulating in fp32. Same

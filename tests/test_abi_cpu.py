@@ -332,11 +332,12 @@ def test_ncssd_arguments(lib):
         assert _call_nc(lib, _nc_launch(), p) == NULL
     assert _call_nc(lib, _nc_launch(), y=0) == NULL
     assert _call_nc(lib, _nc_launch(batch=0), [0] * 4, y=0) == OK
-    # x and y need 16 bytes; bf16 C needs 8; fp32 B and m need 4
-    for i, off in ((0, 8), (2, 4), (1, 2), (3, 2)):
+    # x and y need 16 bytes; C 8 (bf16) or 16 (fp32); fp32 B and m need 4
+    for i, off, io in ((0, 8, binding.VIMSCAN_F32), (2, 4, binding.VIMSCAN_BF16), (2, 8, binding.VIMSCAN_F32),
+                       (1, 2, binding.VIMSCAN_F32), (3, 2, binding.VIMSCAN_F32)):
         p = [0x10000000 * (j + 1) for j in range(4)]
         p[i] += off
-        assert _call_nc(lib, _nc_launch(io_dtype=binding.VIMSCAN_BF16 if i == 2 else binding.VIMSCAN_F32), p) == ALIGN
+        assert _call_nc(lib, _nc_launch(io_dtype=io), p) == ALIGN
     assert _call_nc(lib, _nc_launch(), y=0x7F0000008) == ALIGN
     # y overlapping x, or m
     p = [0x10000000 * (j + 1) for j in range(4)]
