@@ -149,3 +149,74 @@ def ncssd_inputs(batch: int, seqlen: int, d_inner: int, d_state: int = 16, io_dt
     for name in ("x", "B", "C"):
         out[name] = round_to_io(out[name], io_dtype)
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Token orders for the scan in a given order (DefMamba page, section 1: raster, Hilbert curve and
+# local-window scans; section 2.1: deformable re-ranking by per-token index offsets). An order is
+# data: row s lists the token positions 0..T-1 of sequence s in the order the forward scan visits
+# them. Tokens that are not patches of the grid (a class token, auxiliary tokens) keep their
+# place in the order.
+
+
+def _hilbert_xy(n: int, d: int):
+    """Cell (x, y) of step d on the Hilbert curve through an n x n grid, n a power of two: the
+    curve is built quadrant by quadrant, each sub-curve rotated or reflected so its ends meet."""
+    x = y = 0
+    s = 1
+    t = d
+    while s < n:
+        rx = 1 & (t // 2)
+        ry = 1 & (t ^ rx)
+        if ry == 0:
+            if rx == 1:
+                x, y = s - 1 - x, s - 1 - y
+            x, y = y, x
+        x += s * rx
+        y += s * ry
+        t //= 4
+        s *= 2
+    return x, y
+
+
+def grid_order(kind: str, side: int, T: int, window: int = 7) -> np.ndarray:
+    """One sequence's order for a side x side patch grid plus T - side^2 other tokens placed in
+    the middle of the sequence (as Vision Mamba places its class token): 'raster', 'hilbert'
+    (side a power of two), 'local' (window x window blocks in raster order, raster inside each
+    block). Returns int32 (T,)."""
+    P = side * side
+    extra = T - P
+    if extra < 0:
+        raise ValueError("T must hold the grid")
+    mid = P // 2                       # patches before the extra tokens
+    def token_of_patch(p):             # token position of raster patch p
+        return p if p < mid else p + extra
+    if kind == "raster":
+        cells = [(r, c) for r in range(side) for c in range(side)]
+    elif kind == "hilbert":
+        if side & (side - 1):
+            raise ValueError("the Hilbert order needs a power-of-two side")
+        cells = [_hilbert_xy(side, d)[::-1] for d in range(P)]
+    elif kind == "local":
+        cells = [(br + r, bc + c) for br in range(0, side, window) for bc in range(0, side, window)
+                 for r in range(min(window, side - br)) for c in range(min(window, side - bc))]
+    else:
+        raise ValueError(f"unknown order {kind!r}")
+    patches = [token_of_patch(r * side + c) for r, c in cells]
+    order = patches[:mid] + list(range(mid, mid + extra)) + patches[mid:]
+    return np.asarray(order, dtype=np.int32)
+
+
+def deformable_order(T: int, seed: int, scale: float = 8.0) -> np.ndarray:
+    """A re-ranked order: position k gets the key k + scale * tanh(g_k), g_k ~ N(0, 1), and the
+    tokens are visited by increasing key (ties by position) -- the shape of DefMamba's
+    scan-order offsets, drawn at random instead of predicted by a network."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    key = np.arange(T) + scale * np.tanh(rng.standard_normal(T))
+    return np.argsort(key, kind="stable").astype(np.int32)
+
+
+def random_orders(nseq: int, T: int, seed: int) -> np.ndarray:
+    """nseq independent uniformly random permutations of 0..T-1, int32 (nseq, T)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.stack([rng.permutation(T) for _ in range(nseq)]).astype(np.int32).reshape(nseq, T)

@@ -18,8 +18,10 @@ decay examples, and a first-order IIR filter from scipy. The directional convolu
 against torch's conv1d on zero-padded segments and the composed path against the plain scan run
 on the convolved inputs. The NC-SSD global-state form is pinned against the running sums of its
 simplified recurrence in both directions (the bidirectional-sum identity), against the pinned scan
-at A = 0, and by the invariance of its state under a joint reordering of the tokens. No function
-here is parity unpinned.
+at A = 0, and by the invariance of its state under a joint reordering of the tokens. The scan in
+a given token order is pinned against the plain scan run on inputs gathered into that order
+(numpy indexing) and scattered back, and against the reverse order, which swaps the two branches.
+No function here is parity unpinned.
 """
 from __future__ import annotations
 
@@ -69,6 +71,9 @@ def _declare(lib):
                                                   + [_D] * 3 + [ctypes.c_int])
     lib.vimscan_oracle_fwd_f64.restype = ctypes.c_int
     lib.vimscan_oracle_fwd_f64.argtypes = [_D] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_int, _D, ctypes.c_int]
+    lib.vimscan_oracle_bidir_order_f64.restype = ctypes.c_int
+    lib.vimscan_oracle_bidir_order_f64.argtypes = ([_D] * 13 + [ctypes.POINTER(ctypes.c_int32)] + [ctypes.c_int64] * 5
+                                                   + [_D, ctypes.c_int])
     lib.vimscan_oracle_ncssd_f64.restype = ctypes.c_int
     lib.vimscan_oracle_ncssd_f64.argtypes = [_D] * 4 + [ctypes.c_int64] * 5 + [_D, _D, ctypes.c_int]
     return lib
@@ -204,6 +209,28 @@ def fwd(inputs: dict, seg_len: int = 0, swap: bool = False, nthreads: int = 0, l
     y = np.empty((Bsz, L, Di), dtype=np.float64)
     rc = lib.vimscan_oracle_fwd_f64(*[_ptr(a) for a in arrs], Bsz, L, Di, N, int(seg_len), int(bool(swap)), _ptr(y),
                                     int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y
+
+
+def bidir_order_fwd(inputs: dict, order, seg_len: int = 0, nthreads: int = 0, lib=None):
+    """The bidirectional scan in a given token order (DefMamba page, sections 1 and 2.1), in
+    float64: the forward path visits order[s][0..T-1] of every sequence (segment) s, the backward
+    path the same tokens from the end of the list; outputs land at the tokens' own positions.
+    ``inputs`` as ``bidir_fwd``; order (batch * L / T, T) integer, rows permutations of 0..T-1."""
+    lib = lib if lib is not None else _load()
+    arrs = [_f64(inputs[k]) for k in ARG_ORDER]
+    x = arrs[0]
+    Bsz, L, Di = x.shape
+    N = arrs[3].shape[-1]
+    T = seg_len if seg_len > 0 else L
+    ordr = np.ascontiguousarray(np.asarray(order), dtype=np.int32)
+    if ordr.shape != (Bsz * L // max(T, 1), T):
+        raise ValueError(f"order must be (batch * seqlen / T, T) = ({Bsz * L // max(T, 1)}, {T})")
+    y = np.empty((Bsz, L, Di), dtype=np.float64)
+    rc = lib.vimscan_oracle_bidir_order_f64(*[_ptr(a) for a in arrs], ordr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                            Bsz, L, Di, N, int(seg_len), _ptr(y), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return y

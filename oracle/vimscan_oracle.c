@@ -63,6 +63,16 @@
  * B, C [batch][seqlen][d_state]; m [batch][seqlen]; H (optional output)
  * [batch * seqlen / T][d_state][d_inner].
  *
+ * Scan in a given token order (vimscan_oracle_bidir_order_f64; DefMamba page, section 1, the
+ * table of scan orders (raster, Hilbert curve, local windows), and section 2.1, the deformable
+ * scan whose index offsets re-rank the tokens of the sequence): per sequence (segment when
+ * seg_len > 0) an order lists the T token positions in the sequence the scan visits them in.
+ * The forward path visits order[0], order[1], ..., order[T-1]; the backward path visits the same
+ * tokens in the opposite order, order[T-1], ..., order[0]. Each step uses that token's x, dt, B
+ * and C, and each direction's readout lands at the token's own position, so
+ * y[t] = silu(z[t]) * (yf[t] + yb[t]) as before. The raster order order[k] = k is the plain
+ * bidirectional scan. The state starts from zero at the first step of every sequence.
+ *
  * Layouts (row-major, last index fastest):
  *   x, dt, z, y, yf, yb : [batch][seqlen][d_inner]
  *   B_f, C_f, B_b, C_b  : [batch][seqlen][d_state]
@@ -366,6 +376,83 @@ int vimscan_oracle_ncssd_f64(const double* x, const double* Bm, const double* Cm
         }
         free(xm);
         free(h);
+    }
+    return err;
+}
+
+/* Bidirectional scan in the token order of `order` ([batch * seqlen / T][T], every row a
+   permutation of 0..T-1). Returns 0, -1 (bad arguments, including an order entry outside
+   0..T-1) or -2 (no memory). */
+int vimscan_oracle_bidir_order_f64(const double* x, const double* dt, const double* z,
+                                   const double* B_f, const double* C_f, const double* B_b,
+                                   const double* C_b, const double* A_f, const double* A_b,
+                                   const double* D_f, const double* D_b, const double* dt_bias_f,
+                                   const double* dt_bias_b, const int32_t* order, int64_t batch,
+                                   int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                   int64_t seg_len, double* y, int nthreads) {
+    if (!x || !dt || !z || !B_f || !C_f || !B_b || !C_b || !A_f || !A_b || !D_f || !D_b ||
+        !dt_bias_f || !dt_bias_b || !order || !y)
+        return -1;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || seg_len < 0) return -1;
+    if (seg_len > 0 && seqlen % seg_len != 0) return -1;
+    const int64_t Di = d_inner, N = d_state;
+    const int64_t T = seg_len > 0 ? seg_len : seqlen;
+    if (batch == 0 || seqlen == 0 || Di == 0) return 0;
+    const int64_t S = batch * seqlen / T;
+    for (int64_t i = 0; i < S * T; ++i)
+        if (order[i] < 0 || order[i] >= T) return -1;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* h = (double*)malloc(sizeof(double) * (size_t)N);
+        double* of = (double*)malloc(sizeof(double) * (size_t)T);
+        double* ob = (double*)malloc(sizeof(double) * (size_t)T);
+        const int ok = (h && of && ob);
+        if (!ok) {
+#pragma omp atomic write
+            err = -2;
+        }
+#pragma omp for collapse(2) schedule(static)
+        for (int64_t s = 0; s < S; ++s) {
+            for (int64_t d = 0; d < Di; ++d) {
+                if (!ok) continue;
+                const int32_t* ord = order + s * T;
+                for (int dir = 0; dir < 2; ++dir) {
+                    const double* Bm = dir == 0 ? B_f : B_b;
+                    const double* Cm = dir == 0 ? C_f : C_b;
+                    const double* A = dir == 0 ? A_f : A_b;
+                    const double Dd = dir == 0 ? D_f[d] : D_b[d];
+                    const double bias = dir == 0 ? dt_bias_f[d] : dt_bias_b[d];
+                    double* out = dir == 0 ? of : ob;
+                    for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+                    for (int64_t k = 0; k < T; ++k) {
+                        /* forward: the order's k-th token; backward: the same list from its end */
+                        const int64_t t = ord[dir == 0 ? k : T - 1 - k];
+                        const int64_t row = s * T + t;
+                        const double xt = x[row * Di + d];
+                        const double delta = vimscan_oracle_softplus(dt[row * Di + d] + bias);
+                        double acc = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            h[n] = exp(delta * A[d * N + n]) * h[n] + delta * Bm[row * N + n] * xt;
+                            acc += Cm[row * N + n] * h[n];
+                        }
+                        out[t] = acc + Dd * xt;
+                    }
+                }
+                for (int64_t t = 0; t < T; ++t) {
+                    const int64_t i = (s * T + t) * Di + d;
+                    y[i] = vimscan_oracle_silu(z[i]) * (of[t] + ob[t]);
+                }
+            }
+        }
+        free(h);
+        free(of);
+        free(ob);
     }
     return err;
 }
