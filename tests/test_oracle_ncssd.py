@@ -139,8 +139,8 @@ NCSSD_MUTATIONS = {
     "readout_takes_B": ("acc += Cm[(s * T + i) * N + n] * h[n];", "acc += Bm[(s * T + i) * N + n] * h[n];"),
     "state_from_first_token": ("for (int64_t j = 0; j < T; ++j) acc += Bm", "for (int64_t j = 0; j < 1; ++j) acc += Bm"),
     "readout_drops_last_state": ("for (int64_t n = 0; n < N; ++n) acc += Cm", "for (int64_t n = 0; n < N - 1; ++n) acc += Cm"),
-    "segments_ignored": ("const int64_t T = seg_len > 0 ? seg_len : seqlen;\n    if (batch == 0 || seqlen == 0 || Di == 0) return 0;\n    const int64_t S",
-                         "const int64_t T = seqlen;\n    if (batch == 0 || seqlen == 0 || Di == 0) return 0;\n    const int64_t S"),
+    "segments_ignored": ("const int64_t T = seg_len > 0 ? seg_len : seqlen;\n    if (batch == 0 || seqlen == 0 || Di == 0) return 0;\n    const int64_t S = batch * seqlen / T; /* sequences",
+                         "const int64_t T = seqlen;\n    if (batch == 0 || seqlen == 0 || Di == 0) return 0;\n    const int64_t S = batch * seqlen / T; /* sequences"),
 }
 
 
