@@ -50,7 +50,7 @@ class _Conv(ctypes.Structure):
 
 EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_fwd", "vimscan_plan_launch",
             "vimscan_workspace_bytes", "vimscan_status_string", "vimscan_version", "vimscan_ncssd_fwd",
-            "vimscan_ncssd_plan")
+            "vimscan_ncssd_plan", "vimscan_bidir_order_fwd")
 
 
 def lib_path() -> str:
@@ -83,6 +83,8 @@ def load_library():
             lib.vimscan_status_string.argtypes = [ctypes.c_int]
             lib.vimscan_version.restype = ctypes.c_char_p
             lib.vimscan_version.argtypes = []
+            lib.vimscan_bidir_order_fwd.restype = ctypes.c_int
+            lib.vimscan_bidir_order_fwd.argtypes = [vp] * 14 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
             lib.vimscan_ncssd_fwd.restype = ctypes.c_int
             lib.vimscan_ncssd_fwd.argtypes = [vp] * 4 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
             lib.vimscan_ncssd_plan.restype = ctypes.c_int
@@ -143,10 +145,12 @@ class PreparedCall:
 
     def __init__(self, x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
                  out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, stream=None,
-                 conv=None, aux_swap: bool = False, forward_only: bool = False):
+                 conv=None, aux_swap: bool = False, forward_only: bool = False, order=None):
         lib = load_library()
         if forward_only and conv is not None:
             raise ValueError("the forward-only scan takes no convolution")
+        if order is not None and (conv is not None or forward_only):
+            raise ValueError("a scan order goes with the plain bidirectional scan only")
         ios = (x, dt, z, B_f, C_f, B_b, C_b)
         params = (A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b)
         if x.dim() != 3:
@@ -176,6 +180,12 @@ class PreparedCall:
                                      "float32 on x's device")
             cstruct = _Conv(w_f.data_ptr(), b_f.data_ptr(), w_b.data_ptr(), b_b.data_ptr(), K)
             params = params + tuple(conv)
+        if order is not None:
+            T = seg_len if seg_len > 0 else L
+            if (order.device != dev or order.dtype != torch.int32 or not order.is_contiguous()
+                    or tuple(order.shape) != (Bsz * L // max(T, 1), T)):
+                raise ValueError("order must be a contiguous int32 (batch * L / T, T) tensor on x's device")
+            params = params + (order,)
         if out is None:
             out = torch.empty_like(x)
         elif out.device != dev or out.dtype != x.dtype or out.shape != x.shape or not out.is_contiguous():
@@ -199,6 +209,10 @@ class PreparedCall:
             self._fn = lib.vimscan_fwd
             self._args = (tuple(t.data_ptr() for t in (x, dt, z, B_f, C_f, A_f, D_f, dt_bias_f))
                           + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
+        elif order is not None:
+            self._fn = lib.vimscan_bidir_order_fwd
+            self._args = (tuple(t.data_ptr() for t in ios + params)
+                          + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
         elif cstruct is None:
             self._fn = lib.vimscan_bidir_fwd
             self._args = (tuple(t.data_ptr() for t in ios + params)
@@ -221,17 +235,19 @@ class PreparedCall:
 
 def bidir_fwd(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
               out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, conv=None,
-              aux_swap: bool = False):
+              aux_swap: bool = False, order=None):
     """y = silu(z) * (forward selective scan + backward selective scan), on the GPU.
 
     x, dt, z: (B, L, Di); B_*, C_*: (B, L, 16), all float32 or all bfloat16, contiguous, on one
     CUDA(HIP) device. A_*: (Di, 16); D_*, dt_bias_*: (Di,), float32. seg_len: 0, or the period of
     the state reset (must divide L). conv: None, or (w_f, bias_f, w_b, bias_b) float32 taps (Di, K)
     and biases (Di,) of the directional convolution + SiLU in front of each direction
-    (vimscan_bidir_conv_fwd). Returns y (B, L, Di) in x's dtype (``out`` if given).
+    (vimscan_bidir_conv_fwd). order: None, or an int32 (B * L / T, T) tensor whose rows list each
+    sequence's tokens in the order the forward path visits them (vimscan_bidir_order_fwd; T =
+    seg_len or L). Returns y (B, L, Di) in x's dtype (``out`` if given).
     Queued on torch's current stream for x's device; does not synchronise."""
     return PreparedCall(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len, out,
-                        chunk_len, general_decay, workspace, conv=conv, aux_swap=aux_swap)()
+                        chunk_len, general_decay, workspace, conv=conv, aux_swap=aux_swap, order=order)()
 
 
 def prepare_fwd(x, dt, z, B, C, A, D, dt_bias, seg_len: int = 0, out=None, chunk_len: int = 0,

@@ -169,11 +169,19 @@ struct ScanArgs {
     const float* cb[2];  // its biases [Di]
     int conv_k;          // taps, 1..kMaxTaps; 0 without the convolution
     int uni;             // 1: forward only (vimscan_fwd): every wave of a workgroup is a channel block
+    const int32_t* order;  // kOrdered: [nseq][Lp] the token each scan step visits (vimscan_bidir_order_fwd)
 };
 
 // Taps of the directional convolution the kernels carry (a layer with fewer taps is run with
 // the missing ones at zero).
 constexpr int kMaxTaps = 4;
+
+// What a scan kernel instance does besides the plain bidirectional scan.
+enum Variant {
+    kPlain = 0,     // raster order, x as given
+    kWithConv = 1,  // the directional convolution + SiLU in front of each direction
+    kOrdered = 2    // the tokens of every sequence visited in the order of ScanArgs::order
+};
 
 // The state-independent part of one token, computed a token ahead of its state update.
 struct Prelude {
@@ -363,19 +371,24 @@ __device__ __forceinline__ uint32_t ld_global_raw(const void* base, int64_t i) {
 // the three before it in walk order (a register window; at the walk's first step the window is
 // loaded from the tokens before it, which may lie in the neighbouring chunk, and is zero
 // outside the sequence).
-template <typename IO, int kDecay, int kMode, bool kGlobalPark, bool kConv>
+template <typename IO, int kDecay, int kMode, bool kGlobalPark, int kVar>
 __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
                                      const float* lds_c, int kbeg, int kend, float& dsum) {
+    constexpr bool kConv = kVar == kWithConv;
+    constexpr bool kOrd = kVar == kOrdered;
     constexpr int P = kConv ? 3 : 4;  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
     constexpr uint32_t e = IoTraits<IO>::bytes;
     constexpr bool kReadout = kMode != kAggregate;
     using E = typename IoTraits<IO>::elem;
     if (kbeg >= kend) return;
     const int len = c.t1 - c.t0;
-    const int64_t row0 = static_cast<int64_t>(c.seq) * a.Lp + c.t0;  // first token row of the chunk
-    const int64_t eoff = row0 * a.Di;
+    const int64_t row0 = static_cast<int64_t>(c.seq) * a.Lp + c.t0;  // first step (= token row) of the chunk
+    // In a given order the chunk's steps visit tokens anywhere in the sequence: the buffers then
+    // cover the whole sequence and every token row comes from the order.
+    const int64_t rbase = kOrd ? static_cast<int64_t>(c.seq) * a.Lp : row0;
+    const int64_t eoff = rbase * a.Di;
     const uint32_t rowb = static_cast<uint32_t>(a.Di) * e;           // bytes per token row
-    const uint32_t span = static_cast<uint32_t>(len) * rowb;
+    const uint32_t span = static_cast<uint32_t>(kOrd ? a.Lp : len) * rowb;
     const __amdgpu_buffer_rsrc_t rx = chunk_rsrc(static_cast<const E*>(a.x) + eoff, span);
     const __amdgpu_buffer_rsrc_t rd = chunk_rsrc(static_cast<const E*>(a.dt) + eoff, span);
     const __amdgpu_buffer_rsrc_t rz = chunk_rsrc(static_cast<const E*>(a.z) + eoff, span);
@@ -385,7 +398,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const __amdgpu_buffer_rsrc_t rp =
         chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.slot) * a.T * kWave : nullptr,
                    static_cast<uint32_t>(a.T) * kWave * 4);
-    const float* Bs = uniform_ptr(a.Brow[c.dir] + row0 * kN);
+    const float* Bs = uniform_ptr(a.Brow[c.dir] + rbase * kN);
     const uint32_t vo = static_cast<uint32_t>(c.dc) * e;
     const uint32_t vp = static_cast<uint32_t>(c.lane) * 4;
     const int last = kend - 1;
@@ -395,8 +408,18 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const int sgn = 1 - 2 * c.dir;
     const int tbase = c.dir * (len - 1);
     auto lt = [&](int k) { return tbase + sgn * k; };
+    // Token row (from rbase) of walk step min(k, last): the step itself, or in a given order the
+    // token the order lists for it, read through the scalar unit and clamped into the sequence
+    // (an order that is not a permutation gives unspecified outputs but no access outside it).
+    typedef const int32_t __attribute__((address_space(4)))* OrdPtr;
+    const OrdPtr ord = (OrdPtr)uniform_ptr(kOrd ? a.order + row0 : a.order);
+    auto trow = [&](int k) -> int {
+        const int st = lt(min(k, last));
+        if constexpr (kOrd) return min(max(static_cast<int>(ord[st]), 0), a.Lp - 1);
+        else return st;
+    };
     auto toff = [&](int k) {  // token row byte offset of walk step min(k, last)
-        return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lt(min(k, last)))) * rowb;
+        return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(trow(k))) * rowb;
     };
     auto poff = [&](int k) {  // park byte offset of walk step min(k, last)
         return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lt(min(k, last)))) * (kWave * 4);
@@ -441,7 +464,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     // step k. C rows come from the chunk's copy in LDS (staged once per workgroup), read as
     // wave-uniform broadcasts at the start of the step that uses them.
     float Bn[kN], Cv[kN];
-    ld_row(Bs, static_cast<uint32_t>(lt(kbeg)) * (kN * 4), Bn);
+    ld_row(Bs, static_cast<uint32_t>(trow(kbeg)) * (kN * 4), Bn);
     auto lds_row = [&](int k, float (&v)[kN]) {
         const float4* cp = reinterpret_cast<const float4*>(lds_c + lt(min(k, last)) * kN);
 #pragma unroll
@@ -455,7 +478,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     };
     if (kReadout) lds_row(kbeg, Cv);
     Prelude cur = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
-    ld_row(Bs, static_cast<uint32_t>(lt(min(kbeg + 1, last))) * (kN * 4), Bn);
+    ld_row(Bs, static_cast<uint32_t>(trow(kbeg + 1)) * (kN * 4), Bn);
     {
         const uint32_t so = toff(kbeg + P);
         xr[0] = ld_raw(IO{}, rx, vo, so);
@@ -489,7 +512,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
         // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
         const Prelude nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
-        ld_row(Bs, static_cast<uint32_t>(lt(min(kk + 2, last))) * (kN * 4), Bn);
+        ld_row(Bs, static_cast<uint32_t>(trow(kk + 2)) * (kN * 4), Bn);
         if (kMode == kAggregate) dsum += cur.delta2;
         float yv = ln.template update<kReadout>(cur, Cv);
         if (kConv && kReadout) yv = fmaf(ln.Dd, cur.x, yv);  // own skip term on own input u
@@ -508,10 +531,11 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             // the readout stays in the token's single basic block, where it interleaves with the
             // next token's prelude.
             const float ysum = kConv ? yv + other : fmaf(ln.Dsum, cur.x, yv + other);
-            st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * ysum);
+            st_buf(IO{}, ry, vo, kOrd ? toff(kk) : static_cast<uint32_t>(tl) * rowb, silu(zv) * ysum);
         }
         if (kMode == kOut)
-            st_buf(IO{}, ry, vo, static_cast<uint32_t>(tl) * rowb, silu(zv) * (kConv ? yv : fmaf(ln.Dd, cur.x, yv)));
+            st_buf(IO{}, ry, vo, kOrd ? toff(kk) : static_cast<uint32_t>(tl) * rowb,
+                   silu(zv) * (kConv ? yv : fmaf(ln.Dd, cur.x, yv)));
         cur = nxt;
         if (kReadout) {
 #pragma unroll
@@ -534,15 +558,15 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
 }
 
 // The walk instance for this wave's transition form (wave-uniform).
-template <typename IO, int kMode, bool kGlobalPark, bool kConv>
+template <typename IO, int kMode, bool kGlobalPark, int kVar>
 __device__ __forceinline__ void walk_as(int form, const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
                                         const float* lds_c, int kbeg, int kend, float& dsum) {
     if (form == kGeometric)
-        walk<IO, kGeometric, kMode, kGlobalPark, kConv>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+        walk<IO, kGeometric, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
     else if (form == kProgression)
-        walk<IO, kProgression, kMode, kGlobalPark, kConv>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+        walk<IO, kProgression, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
     else
-        walk<IO, kGeneral, kMode, kGlobalPark, kConv>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+        walk<IO, kGeneral, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
 }
 
 // Widen the bf16 B rows to fp32 rows once per call: [B_f, B_b][tokens][16], read through the
@@ -624,16 +648,45 @@ __device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& 
     }
 }
 
+// The same for a scan in a given order: the chunk's C rows are gathered in step order (row k of
+// direction dir in LDS is the C row of the token the order lists for step t0 + k), so the walk
+// reads them exactly as in raster order. One 32-bit word per thread and pass.
+template <typename IO>
+__device__ __forceinline__ void stage_c_rows_ordered(const ScanArgs& a, const WgCoords& c, float* lds_c) {
+    constexpr int kPerWord = 4 / IoTraits<IO>::bytes;
+    constexpr int wpr = kN / kPerWord;  // words per row
+    const int len = c.t1 - c.t0;
+    const int64_t srow = static_cast<int64_t>(c.seq) * a.Lp;
+    const int32_t* ord = a.order + srow + c.t0;
+    const int nw = 2 * len * wpr;
+    for (int i = static_cast<int>(threadIdx.x); i < nw; i += static_cast<int>(blockDim.x)) {
+        const int dir = i / (len * wpr);
+        const int k = (i / wpr) % len, w = i % wpr;
+        const int tok = min(max(static_cast<int>(ord[k]), 0), a.Lp - 1);
+        const uint32_t u = reinterpret_cast<const uint32_t*>(
+            static_cast<const typename IoTraits<IO>::elem*>(a.Cm[dir]) + (srow + tok) * kN)[w];
+        float* dst = lds_c + dir * a.T * kN + k * kN + w * kPerWord;
+        if (kPerWord == 1) {
+            dst[0] = __uint_as_float(u) * kLn2;
+        } else {
+            dst[0] = __uint_as_float(u << 16) * kLn2;
+            dst[1] = __uint_as_float(u & 0xffff0000u) * kLn2;
+        }
+    }
+}
+
 // Main scan: one chunk of one sequence, 64 channels; wave 0 forward, wave 1 backward. The waves
 // meet in the middle of the chunk through the park (LDS, or a global scratch region per
 // workgroup when the chunk is long; see the file header).
-template <typename IO, bool kCarry, bool kGlobalPark, bool kConv>
+template <typename IO, bool kCarry, bool kGlobalPark, int kVar>
 __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
+    constexpr bool kConv = kVar == kWithConv;
     extern __shared__ float lds[];  // C rows [2][T][16], then the park [subs][T][64] when in LDS
     const WgCoords c = wg_coords(a, false);
     float* lds_c = lds + c.dir * a.T * kN;
     float* lds_park = lds + 2 * a.T * kN + c.sub * a.T * kWave;
-    stage_c_rows<IO>(a, c, lds, false);
+    if constexpr (kVar == kOrdered) stage_c_rows_ordered<IO>(a, c, lds);
+    else stage_c_rows<IO>(a, c, lds, false);
     Lane ln;
     ln.init(a, c.dir, c.dc, kConv);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
@@ -651,9 +704,9 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
     float unused = 0.0f;
     __syncthreads();  // the C rows are staged
-    walk_as<IO, kPark, kGlobalPark, kConv>(form, a, c, ln, lds_park, lds_c, 0, n1, unused);
+    walk_as<IO, kPark, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, 0, n1, unused);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
-    walk_as<IO, kFinish, kGlobalPark, kConv>(form, a, c, ln, lds_park, lds_c, n1, len, unused);
+    walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, n1, len, unused);
 }
 
 // Forward-only scan (vimscan_fwd): one chunk of one sequence, every wave a channel block of 64,
@@ -676,13 +729,14 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
     const int form = ln.decay_form(a, 0, c.dc);
     float unused = 0.0f;
     __syncthreads();  // the C rows are staged
-    walk_as<IO, kOut, false, false>(form, a, c, ln, nullptr, lds, 0, c.t1 - c.t0, unused);
+    walk_as<IO, kOut, false, kPlain>(form, a, c, ln, nullptr, lds, 0, c.t1 - c.t0, unused);
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
 // from a zero state, and the sum of delta over the chunk.
-template <typename IO, bool kConv>
+template <typename IO, int kVar>
 __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
+    constexpr bool kConv = kVar == kWithConv;
     const WgCoords c = wg_coords(a, a.uni != 0);
     Lane ln;
     ln.init(a, c.dir, c.dc, false);
@@ -692,7 +746,7 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     const int form = ln.decay_form(a, c.dir, c.dc);
     const int len = c.t1 - c.t0;
     float s = 0.0f;
-    walk_as<IO, kAggregate, false, kConv>(form, a, c, ln, nullptr, nullptr, 0, len, s);
+    walk_as<IO, kAggregate, false, kVar>(form, a, c, ln, nullptr, nullptr, 0, len, s);
     if (c.valid) {
         const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
         float* dst = a.carry + slot * kN * a.Di;
@@ -867,15 +921,15 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // Threads per workgroup: two waves (forward, backward) per channel block, or one forward only.
 unsigned wg_threads(const Plan& p) { return static_cast<unsigned>((p.uni ? 64 : 128) * p.subs); }
 
-template <typename IO, bool kGlobalPark, bool kConv>
+template <typename IO, bool kGlobalPark, int kVar>
 void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
     const dim3 grid(static_cast<unsigned>(p.wgs)), block(wg_threads(p));
     const size_t lds = (2 * p.T * kN + (kGlobalPark ? 0 : p.subs * p.T * kWave)) * sizeof(float);
-    if (carry) hipLaunchKernelGGL((k_bidir_scan<IO, true, kGlobalPark, kConv>), grid, block, lds, s, a);
-    else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark, kConv>), grid, block, lds, s, a);
+    if (carry) hipLaunchKernelGGL((k_bidir_scan<IO, true, kGlobalPark, kVar>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark, kVar>), grid, block, lds, s, a);
 }
 
-template <typename IO, bool kConv>
+template <typename IO, int kVar>
 int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (p.widen) {
         if (aligned(a.Bm[0], 16) && aligned(a.Bm[1], 16)) {
@@ -887,7 +941,7 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
         }
     }
     if (p.K > 1) {
-        hipLaunchKernelGGL((k_chunk_aggregate<IO, kConv>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), 0,
+        hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), 0,
                            s, a);
         const dim3 cgrid(static_cast<unsigned>(p.ncb), 4, static_cast<unsigned>((p.uni ? 1 : 2) * p.nseq));
         hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
@@ -901,9 +955,9 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
         else hipLaunchKernelGGL((k_fwd_scan<IO, false>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), lds,
                                 s, a);
     } else if (p.park_global) {
-        launch_scan<IO, true, kConv>(a, p, s, p.K > 1);
+        launch_scan<IO, true, kVar>(a, p, s, p.K > 1);
     } else {
-        launch_scan<IO, false, kConv>(a, p, s, p.K > 1);
+        launch_scan<IO, false, kVar>(a, p, s, p.K > 1);
     }
     if (hipGetLastError() != hipSuccess) return VIMSCAN_ERR_HIP;
     if (timed && hipEventRecord(ev1, s) != hipSuccess) return VIMSCAN_ERR_HIP;
@@ -915,11 +969,12 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
     return VIMSCAN_OK;
 }
 
-// Both entry points: conv is NULL for the plain scan.
+// Every entry point: conv is NULL without the convolution, order NULL in raster order (not both
+// set).
 int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, const void* C_f, const void* B_b,
                const void* C_b, const float* A_f, const float* A_b, const float* D_f, const float* D_b,
-               const float* dt_bias_f, const float* dt_bias_b, const vimscan_conv* conv, int64_t seg_len, void* y,
-               const vimscan_launch* launch) {
+               const float* dt_bias_f, const float* dt_bias_b, const vimscan_conv* conv, const int32_t* order,
+               int64_t seg_len, void* y, const vimscan_launch* launch) {
     if (!launch) return VIMSCAN_ERR_NULL;
     Plan p;
     int rc = make_plan(launch, seg_len, &p);
@@ -931,6 +986,9 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
         return VIMSCAN_ERR_NULL;
     if (conv && (!conv->w_f || !conv->bias_f || !conv->w_b || !conv->bias_b)) return VIMSCAN_ERR_NULL;
     const size_t e = launch->io_dtype == VIMSCAN_F32 ? 4 : 2;
+    // in a given order a walk's buffers span a whole sequence, addressed with 32-bit offsets
+    if (order && static_cast<uint64_t>(p.Lp) * static_cast<uint64_t>(launch->d_inner) * e >= (uint64_t(1) << 32))
+        return VIMSCAN_ERR_SHAPE;
     const void* io[] = {x, dt, z, y};
     for (const void* q : io)
         if (!aligned(q, e)) return VIMSCAN_ERR_ALIGN;
@@ -949,13 +1007,15 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     for (const auto& in : ins)
         if (overlaps(y, S * e, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
     const size_t nw = conv ? static_cast<size_t>(launch->d_inner) * static_cast<size_t>(conv->k) * 4 : 0;
+    const size_t nord = order ? static_cast<size_t>(launch->batch) * launch->seqlen * 4 : 0;
     const struct {
         const void* p;
         size_t n;
     } cins[] = {{conv ? conv->w_f : nullptr, nw},
                 {conv ? conv->bias_f : nullptr, nw ? nd : 0},
                 {conv ? conv->w_b : nullptr, nw},
-                {conv ? conv->bias_b : nullptr, nw ? nd : 0}};
+                {conv ? conv->bias_b : nullptr, nw ? nd : 0},
+                {order, nord}};
     for (const auto& in : cins) {
         if (in.n && !aligned(in.p, 4)) return VIMSCAN_ERR_ALIGN;
         if (overlaps(y, S * e, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
@@ -1012,15 +1072,19 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.cb[1] = conv ? conv->bias_b : nullptr;
     a.conv_k = conv ? static_cast<int>(conv->k) : 0;
     a.uni = p.uni ? 1 : 0;
+    a.order = order;
     hipStream_t s = static_cast<hipStream_t>(launch->stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(launch->scan_events[0]);
     hipEvent_t ev1 = static_cast<hipEvent_t>(launch->scan_events[1]);
     if (conv)
-        rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float, true>(a, p, s, ev0, ev1)
-                                             : launch_all<Bf16, true>(a, p, s, ev0, ev1);
+        rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float, kWithConv>(a, p, s, ev0, ev1)
+                                             : launch_all<Bf16, kWithConv>(a, p, s, ev0, ev1);
+    else if (order)
+        rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float, kOrdered>(a, p, s, ev0, ev1)
+                                             : launch_all<Bf16, kOrdered>(a, p, s, ev0, ev1);
     else
-        rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float, false>(a, p, s, ev0, ev1)
-                                             : launch_all<Bf16, false>(a, p, s, ev0, ev1);
+        rc = launch->io_dtype == VIMSCAN_F32 ? launch_all<float, kPlain>(a, p, s, ev0, ev1)
+                                             : launch_all<Bf16, kPlain>(a, p, s, ev0, ev1);
     return rc;
 }
 
@@ -1066,7 +1130,7 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
                       const float* D_b, const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
                       const vimscan_launch* launch) {
     if (launch && (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY)) return VIMSCAN_ERR_FLAGS;
-    return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, nullptr, seg_len, y,
+    return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, nullptr, nullptr, seg_len, y,
                       launch);
 }
 
@@ -1076,7 +1140,7 @@ int vimscan_fwd(const void* x, const void* dt, const void* z, const void* B, con
     vimscan_launch l = *launch;
     l.flags |= VIMSCAN_FLAG_FORWARD_ONLY;
     // the forward parameters fill both direction slots; the forward-only kernels read slot 0
-    return bidir_impl(x, dt, z, B, C, B, C, A, A, D, D, dt_bias, dt_bias, nullptr, seg_len, y, &l);
+    return bidir_impl(x, dt, z, B, C, B, C, A, A, D, D, dt_bias, dt_bias, nullptr, nullptr, seg_len, y, &l);
 }
 
 int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* dt, const void* z,
@@ -1086,8 +1150,21 @@ int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* 
     if (!launch || !conv) return VIMSCAN_ERR_NULL;
     if (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY) return VIMSCAN_ERR_FLAGS;
     if (conv->k < 1 || conv->k > kMaxTaps) return VIMSCAN_ERR_CONV;
-    return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, conv, seg_len, y,
+    return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, conv, nullptr, seg_len, y,
                       launch);
+}
+
+int vimscan_bidir_order_fwd(const void* x, const void* dt, const void* z, const void* B_f, const void* C_f,
+                            const void* B_b, const void* C_b, const float* A_f, const float* A_b, const float* D_f,
+                            const float* D_b, const float* dt_bias_f, const float* dt_bias_b, const int32_t* order,
+                            int64_t seg_len, void* y, const vimscan_launch* launch) {
+    if (!launch) return VIMSCAN_ERR_NULL;
+    if (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY) return VIMSCAN_ERR_FLAGS;
+    const bool empty = launch->batch == 0 || launch->seqlen == 0 || launch->d_inner == 0;
+    if (!order && !empty) return VIMSCAN_ERR_NULL;
+    if (order && !aligned(order, 4)) return VIMSCAN_ERR_ALIGN;
+    return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, nullptr, order, seg_len,
+                      y, launch);
 }
 
 }  // extern "C"

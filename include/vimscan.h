@@ -80,8 +80,8 @@ enum vimscan_io_dtype { VIMSCAN_F32 = 0, VIMSCAN_BF16 = 1 };
    (one more small kernel on the stream). For every entry point. */
 #define VIMSCAN_FLAG_AUX_SWAP 2
 /* The launch describes a forward-only call (vimscan_fwd). vimscan_fwd implies it; the planning
-   functions need it to size the forward-only plan; vimscan_bidir_fwd and vimscan_bidir_conv_fwd
-   reject it (VIMSCAN_ERR_FLAGS). */
+   functions need it to size the forward-only plan; vimscan_bidir_fwd, vimscan_bidir_conv_fwd and
+   vimscan_bidir_order_fwd reject it (VIMSCAN_ERR_FLAGS). */
 #define VIMSCAN_FLAG_FORWARD_ONLY 4
 
 /* Shape and launch description, passed by pointer to every entry point. */
@@ -174,6 +174,31 @@ int vimscan_bidir_conv_fwd(const void* x, const vimscan_conv* conv, const void* 
                            const float* A_f, const float* A_b, const float* D_f, const float* D_b,
                            const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
                            const vimscan_launch* launch);
+
+/*
+ * The bidirectional scan in a given token order (DefMamba page: section 1 compares raster,
+ * Hilbert-curve and local-window scan orders; section 2.1 re-ranks the tokens of the sequence by
+ * per-token index offsets). order is device memory, int32 [batch * seqlen / T][T] with T =
+ * seg_len (or seqlen when seg_len is 0): row s lists the token positions 0..T-1 of sequence
+ * (segment) s in the order the forward path visits them; the backward path visits the same
+ * tokens from the end of the list. Every step reads its token's x, dt, B and C, and each
+ * direction's output lands at the token's own position:
+ *   forward:  h at step k uses token order[s][k], k = 0..T-1
+ *   backward: g at step k uses token order[s][k], k = T-1..0
+ *   y[b,t,d] = silu(z[b,t,d]) * (yf_t + yb_t) with yf_t, yb_t the readouts at token t.
+ * The raster order order[s][k] = k gives vimscan_bidir_fwd's result. Rows must be permutations;
+ * entries outside 0..T-1 are clamped into the sequence (unspecified outputs, no access outside
+ * the arrays). order must be 4-byte aligned (VIMSCAN_ERR_ALIGN) and must not overlap y or the
+ * workspace (VIMSCAN_ERR_ALIAS); NULL is VIMSCAN_ERR_NULL unless the call is empty. Everything
+ * else -- layouts, reset, dtypes, plan and workspace -- is that of vimscan_bidir_fwd, plus
+ * VIMSCAN_ERR_SHAPE when T * d_inner * (io element size) >= 2^32 (a walk addresses a whole
+ * sequence with 32-bit offsets).
+ */
+int vimscan_bidir_order_fwd(const void* x, const void* dt, const void* z, const void* B_f,
+                            const void* C_f, const void* B_b, const void* C_b, const float* A_f,
+                            const float* A_b, const float* D_f, const float* D_b,
+                            const float* dt_bias_f, const float* dt_bias_b, const int32_t* order,
+                            int64_t seg_len, void* y, const vimscan_launch* launch);
 
 /*
  * Unidirectional scan (SF-Mamba page: Vim with a one-way scan and auxiliary patch swap): only

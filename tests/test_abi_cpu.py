@@ -347,3 +347,27 @@ def test_ncssd_arguments(lib):
     assert _call_nc(lib, _nc_launch(seqlen=64, chunk_len=16)) == WORKSPACE
     launch = _nc_launch(seqlen=64, chunk_len=16, workspace=0x50000000, workspace_bytes=16)
     assert _call_nc(lib, launch) == WORKSPACE
+
+
+def _call_ord(lib, launch, ptrs=None, order=0x70000000, seg_len=0, y=None):
+    p = ptrs or [0x10000000 * (i + 1) for i in range(13)]
+    y = 0x7F0000000 if y is None else y
+    return lib.vimscan_bidir_order_fwd(*p, order, seg_len, y, ctypes.byref(launch) if launch is not None else None)
+
+
+def test_order_arguments(lib):
+    assert _call_ord(lib, None) == NULL
+    assert _call_ord(lib, _launch(), order=0) == NULL
+    assert _call_ord(lib, _launch(batch=0), [0] * 13, order=0, y=0) == OK
+    assert _call_ord(lib, _launch(), order=0x70000002) == ALIGN
+    assert _call_ord(lib, _launch(d_state=8)) == SHAPE
+    assert _call_ord(lib, _launch(seqlen=12), seg_len=5) == SEGLEN
+    launch = _launch()
+    launch.flags = binding.VIMSCAN_FLAG_FORWARD_ONLY
+    assert _call_ord(lib, launch) == FLAGS
+    # y overlapping the order (2 x 12 int32)
+    assert _call_ord(lib, _launch(), y=0x70000000 - 64) == ALIAS
+    # a walk in a given order spans a whole sequence: 2^18 tokens x 4096 fp32 channels is 4 GiB
+    assert _call_ord(lib, _launch(batch=1, seqlen=1 << 18, d_inner=4096)) == SHAPE
+    # the same shape in raster order passes the shape check (and then needs its workspace)
+    assert _call(lib, _launch(batch=1, seqlen=1 << 18, d_inner=4096)) == WORKSPACE
