@@ -10,7 +10,7 @@ Also reported: the dominant kernel's ALU roofline (the scan's exponentials and f
 bind before HBM does; that kernel is timed alone with HIP events the library records around it),
 the same path with the per-state exponential forced (general_decay), the directional convolution
 fused in front (conv_fused), the forward-only scan with and without the auxiliary-token swap, the
-NC-SSD global-state form on the same shape (ncssd: an HBM roofline, on the matrix cores), and the
+scan in a given token order (ordered: local windows of the patch grid), the NC-SSD global-state form on the same shape (ncssd: an HBM roofline, on the matrix cores), and the
 float64 CPU oracle timed on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
@@ -145,6 +145,8 @@ def main(argv=None):
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward-only scan measurements (with and without the auxiliary swap)")
     ap.add_argument("--no-ncssd", action="store_true", help="skip the NC-SSD global-state form measurement")
+    ap.add_argument("--no-order", action="store_true",
+                    help="skip the scan in a given token order (7 x 7 local windows of the patch grid)")
     ap.add_argument("--only-ncssd", action="store_true",
                     help="measure only the NC-SSD global-state form (for its counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -198,6 +200,17 @@ def main(argv=None):
         calls[name] = [binding.prepare_fwd(copies[i][0], copies[i][1], copies[i][2], copies[i][3], copies[i][4],
                                            params[0], params[2], params[4], seg_len=w.seg_len, out=outs[i],
                                            aux_swap=swap) for i in range(ncopy)]
+
+    # the same scan in a given token order: local windows of the patch grid (the grid is the
+    # largest square the sequence holds; the remaining tokens keep their place)
+    from bidirectional_selective_scan_amd.inputs import grid_order
+    T = w.seg_len or w.seqlen
+    side = int(np.sqrt(T - 1)) if T > 1 else 1
+    order_np = np.tile(grid_order("local", side, T, window=max(1, (side + 1) // 2)), (w.batch * w.seqlen // T, 1))
+    order = torch.from_numpy(np.ascontiguousarray(order_np, dtype=np.int32)).to(dev)
+    calls["order"] = [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
+                                           order=order) for i in range(ncopy)]
+    order_desc = f"{side} x {side} patch grid in {max(1, (side + 1) // 2)} x {max(1, (side + 1) // 2)} local windows"
 
     # NC-SSD on inputs of the same shape: x, B, C in the io dtype, m fp32
     from bidirectional_selective_scan_amd.inputs import ncssd_inputs
@@ -327,6 +340,15 @@ def main(argv=None):
                                                                          if name == "fwd_swap" else ""),
                           "value": round(fbytes * args.steps / wall_f / 1e9, 2), "unit": "GB/s",
                           "call_us": stats_us(per_call_f), "kernel_us": round(float(np.mean(per_scan_f)) * 1e6, 3)}
+    if not args.no_order:
+        wall_o, per_call_o, per_scan_o = timed("order")
+        ko = float(np.mean(per_scan_o))
+        obytes = nbytes + w.batch * w.seqlen * 4   # plus the order
+        out["ordered"] = {"what": "the same scan in a given token order (vimscan_bidir_order_fwd): " + order_desc,
+                          "value": round(obytes * args.steps / wall_o / 1e9, 2), "unit": "GB/s",
+                          "call_us": stats_us(per_call_o), "kernel_us": round(ko * 1e6, 3),
+                          "alu_achieved_tops": round(ops / ko / 1e12, 3),
+                          "alu_frac": round(ops / ko / 1e12 / VALU_PEAK_TOPS, 4)}
     if not args.no_ncssd:
         out["ncssd"] = ncssd_leg(w, timed, stats_us, calls["ncssd"][0].plan, nc_bytes, nc_copies)
     if not args.no_cpu:

@@ -156,10 +156,12 @@ def main():
             lines += ["", "bench.py in the traced run (HIP events the library records around the scan kernel):",
                       f"  automatic transitions   kernel_us mean {b['kernel_us']:.3f}, "
                       f"median {b['scan_kernel_us']['median']:.3f}"]
-            if "general_decay" in b:
-                lines.append(f"  forced general          kernel_us mean {b['general_decay']['kernel_us']:.3f}")
-            if "conv_fused" in b:
-                lines.append(f"  with the convolution    kernel_us mean {b['conv_fused']['kernel_us']:.3f}")
+            labels = {"general_decay": "forced general", "conv_fused": "with the convolution",
+                      "forward_only": "forward only", "forward_only_aux_swap": "forward only + swap",
+                      "ordered": "in a given order", "ncssd": "NC-SSD (whole call)"}
+            for key, label in labels.items():
+                if key in b:
+                    lines.append(f"  {label:23s} kernel_us mean {b[key]['kernel_us']:.3f}")
         open(a.out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
