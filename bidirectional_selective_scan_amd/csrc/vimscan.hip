@@ -42,6 +42,11 @@
 //    only when every lane's row qualifies; VIMSCAN_FLAG_GENERAL_DECAY turns it off.
 //  * Workgroup ids are remapped so that consecutive logical workgroups (which share a
 //    sequence's B/C rows) land on the same XCD and its L2.
+//  * Variants of the same kernels (a template parameter): the directional convolution in front
+//    of each direction (a register window of the previous raw inputs in walk order), and the scan
+//    in a given token order (a step's token is looked up in the order through the scalar unit;
+//    chunks are ranges of steps, C rows are gathered into LDS in step order, so the park, the
+//    meeting point and the chunk carries stay indexed by step).
 
 #include <hip/hip_runtime.h>
 
@@ -411,12 +416,18 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     // Token row (from rbase) of walk step min(k, last): the step itself, or in a given order the
     // token the order lists for it, read through the scalar unit and clamped into the sequence
     // (an order that is not a permutation gives unspecified outputs but no access outside it).
+    // The order entry is read with a 32-bit byte offset, which the scalar load takes as its offset
+    // operand (no 64-bit address arithmetic per step).
     typedef const int32_t __attribute__((address_space(4)))* OrdPtr;
-    const OrdPtr ord = (OrdPtr)uniform_ptr(kOrd ? a.order + row0 : a.order);
+    const char* ordb = reinterpret_cast<const char*>(uniform_ptr(kOrd ? a.order + row0 : a.order));
     auto trow = [&](int k) -> int {
         const int st = lt(min(k, last));
-        if constexpr (kOrd) return min(max(static_cast<int>(ord[st]), 0), a.Lp - 1);
-        else return st;
+        if constexpr (kOrd) {
+            const OrdPtr p = (OrdPtr)(ordb + static_cast<uint32_t>(st) * 4u);
+            return min(max(static_cast<int>(*p), 0), a.Lp - 1);
+        } else {
+            return st;
+        }
     };
     auto toff = [&](int k) {  // token row byte offset of walk step min(k, last)
         return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(trow(k))) * rowb;
@@ -449,9 +460,21 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     };
 
     uint32_t xr[P], dr[P], zr[P], pr[P];
+    // In a given order each step's token is looked up once, when its x and dt are requested, and
+    // rides along the rings: tx[s] is the token whose x/dt slot s holds, tz[s] the one whose z
+    // slot s holds (its y store offset). At the start of step kbeg + r, slot (r + i) % P of tx
+    // holds step kbeg + r + i (i = 1..P-1) and slot r % P step kbeg + r + P.
+    int tx[P], tz[P];
+    auto tokoff = [&](int t) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(t)) * rowb; };
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-        const uint32_t so = toff(kbeg + j);
+        uint32_t so;
+        if constexpr (kOrd) {
+            tx[j] = tz[j] = trow(kbeg + j);
+            so = tokoff(tx[j]);
+        } else {
+            so = toff(kbeg + j);
+        }
         xr[j] = ld_raw(IO{}, rx, vo, so);
         dr[j] = ld_raw(IO{}, rd, vo, so);
         if (kMode == kFinish || kMode == kOut) {
@@ -464,7 +487,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     // step k. C rows come from the chunk's copy in LDS (staged once per workgroup), read as
     // wave-uniform broadcasts at the start of the step that uses them.
     float Bn[kN], Cv[kN];
-    ld_row(Bs, static_cast<uint32_t>(trow(kbeg)) * (kN * 4), Bn);
+    ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[0] : trow(kbeg)) * (kN * 4), Bn);
     auto lds_row = [&](int k, float (&v)[kN]) {
         const float4* cp = reinterpret_cast<const float4*>(lds_c + lt(min(k, last)) * kN);
 #pragma unroll
@@ -478,9 +501,15 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     };
     if (kReadout) lds_row(kbeg, Cv);
     Prelude cur = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
-    ld_row(Bs, static_cast<uint32_t>(trow(kbeg + 1)) * (kN * 4), Bn);
+    ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[1 % P] : trow(kbeg + 1)) * (kN * 4), Bn);
     {
-        const uint32_t so = toff(kbeg + P);
+        uint32_t so;
+        if constexpr (kOrd) {
+            tx[0] = trow(kbeg + P);
+            so = tokoff(tx[0]);
+        } else {
+            so = toff(kbeg + P);
+        }
         xr[0] = ld_raw(IO{}, rx, vo, so);
         dr[0] = ld_raw(IO{}, rd, vo, so);
     }
@@ -501,18 +530,32 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
         asm volatile("" ::"v"(xn), "v"(dn), "v"(zv), "v"(pv) : "memory");
         {
-            const uint32_t so = toff(kk + 1 + P);
+            uint32_t so;
+            if constexpr (kOrd) {
+                tx[jn] = trow(kk + 1 + P);
+                so = tokoff(tx[jn]);
+            } else {
+                so = toff(kk + 1 + P);
+            }
             xr[jn] = ld_raw(IO{}, rx, vo, so);
             dr[jn] = ld_raw(IO{}, rd, vo, so);
         }
+        int ytok = 0;  // kOrd: this step's token (its y store)
         if (kMode == kFinish || kMode == kOut) {
-            const uint32_t so = toff(kk + P);
+            uint32_t so;
+            if constexpr (kOrd) {
+                ytok = tz[j];
+                tz[j] = tx[j];  // step kk + P
+                so = tokoff(tz[j]);
+            } else {
+                so = toff(kk + P);
+            }
             zr[j] = ld_raw(IO{}, rz, vo, so);
             if (kMode == kFinish && kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
         // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
         const Prelude nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
-        ld_row(Bs, static_cast<uint32_t>(trow(kk + 2)) * (kN * 4), Bn);
+        ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[(j + 2) % P] : trow(kk + 2)) * (kN * 4), Bn);
         if (kMode == kAggregate) dsum += cur.delta2;
         float yv = ln.template update<kReadout>(cur, Cv);
         if (kConv && kReadout) yv = fmaf(ln.Dd, cur.x, yv);  // own skip term on own input u
@@ -531,10 +574,10 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             // the readout stays in the token's single basic block, where it interleaves with the
             // next token's prelude.
             const float ysum = kConv ? yv + other : fmaf(ln.Dsum, cur.x, yv + other);
-            st_buf(IO{}, ry, vo, kOrd ? toff(kk) : static_cast<uint32_t>(tl) * rowb, silu(zv) * ysum);
+            st_buf(IO{}, ry, vo, kOrd ? tokoff(ytok) : static_cast<uint32_t>(tl) * rowb, silu(zv) * ysum);
         }
         if (kMode == kOut)
-            st_buf(IO{}, ry, vo, kOrd ? toff(kk) : static_cast<uint32_t>(tl) * rowb,
+            st_buf(IO{}, ry, vo, kOrd ? tokoff(ytok) : static_cast<uint32_t>(tl) * rowb,
                    silu(zv) * (kConv ? yv : fmaf(ln.Dd, cur.x, yv)));
         cur = nxt;
         if (kReadout) {
@@ -821,7 +864,8 @@ constexpr int64_t kUniTarget = 3072;
 const char* const kStatusText[] = {
     "ok",
     "a required pointer is NULL",
-    "bad shape: sizes must be >= 0, d_state must be 16, d_inner < 2^22, batch*seqlen*d_inner < 2^31",
+    "bad shape: a size < 0, batch*seqlen*d_inner >= 2^31, d_inner >= 2^22, or d_state / d_inner not accepted by "
+    "the entry point (16 for the scans; 16, 32 or 64 with d_inner % 16 == 0 for NC-SSD)",
     "bad seg_len: must be 0 or a positive divisor of seqlen",
     "bad io_dtype: must be VIMSCAN_F32 or VIMSCAN_BF16",
     "misaligned pointer",

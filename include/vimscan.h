@@ -1,5 +1,7 @@
 /*
- * vimscan.h -- C ABI of the bidirectional selective scan on AMD MI355X (gfx950).
+ * vimscan.h -- C ABI of the bidirectional selective scan on AMD MI355X (gfx950), with its
+ * variants (directional convolution in front, forward only with the auxiliary swap, a given token
+ * order) and the NC-SSD global-state form (declared further down).
  *
  * The operation (Vision Mamba page, section 2.2 "bidirectional state-space modelling": a
  * forward path over the tokens in raster order and a backward path over them in reverse, the
@@ -52,8 +54,9 @@ extern "C" {
 enum vimscan_status {
     VIMSCAN_OK = 0,
     VIMSCAN_ERR_NULL = -1,      /* a required pointer is NULL (launch, an input, or y) */
-    VIMSCAN_ERR_SHAPE = -2,     /* batch, seqlen or d_inner < 0; d_state != 16;
-                                   d_inner >= 2^22; or batch*seqlen*d_inner >= 2^31 */
+    VIMSCAN_ERR_SHAPE = -2,     /* batch, seqlen or d_inner < 0; d_inner >= 2^22;
+                                   batch*seqlen*d_inner >= 2^31; d_state != 16 for the scans;
+                                   for NC-SSD d_state not 16, 32 or 64 or d_inner % 16 != 0 */
     VIMSCAN_ERR_SEGLEN = -3,    /* seg_len < 0, or seg_len > 0 and seqlen % seg_len != 0 */
     VIMSCAN_ERR_DTYPE = -4,     /* io_dtype is not VIMSCAN_F32 or VIMSCAN_BF16 */
     VIMSCAN_ERR_ALIGN = -5,     /* a pointer is not aligned: x, dt, z, y to the io element
