@@ -200,3 +200,16 @@ def test_b_rows_not_16_byte_aligned():
     y1 = run_gpu(dev)
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     assert_close(to_f64(y1), oracle.bidir_fwd(inp), "bf16", "unaligned B")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("B,L,Di,params", [(1, 32768, 64, "random"),   # 1024 chunks: a long carry chain
+                                           (1, 32768, 64, "s4d"),
+                                           (2, 64, 4096, "random"),    # wide: 64 channel blocks
+                                           (1, 3, 8192, "s4d")])
+def test_long_and_wide_extremes(B, L, Di, params, io):
+    inp = _case(B, L, Di, io, seed=B + L + Di, params=params)
+    dev = to_device(inp, io)
+    info = binding.launch_info(B, L, Di, 16, 0, io)
+    y = to_f64(run_gpu(dev))
+    assert_close(y, oracle.bidir_fwd(inp, nthreads=16), io, f"B={B} L={L} Di={Di} {params} plan={info}")
