@@ -486,6 +486,13 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     // B rows (SGPRs) run one token ahead: B(k+1) is consumed by the prelude of token k+1 during
     // step k. C rows come from the chunk's copy in LDS (staged once per workgroup), read as
     // wave-uniform broadcasts at the start of the step that uses them.
+    // The current and the next token's prelude live in two buffers used alternately by the parity
+    // of the walk step (a compile-time index in the unrolled loop), so the 34 values are not copied
+    // from "next" to "current" between tokens (the register allocator could not line the copies up
+    // with the loop-carried registers). Only the plain bf16 instances do this: the convolution and
+    // ordered variants have no registers for a second prelude at 3 waves per SIMD (168 VGPRs), and
+    // the fp32 instances measured no faster (slower with general transitions).
+    constexpr bool kDB = kVar == kPlain && IoTraits<IO>::bytes == 2;
     float Bn[kN], Cv[kN];
     ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[0] : trow(kbeg)) * (kN * 4), Bn);
     auto lds_row = [&](int k, float (&v)[kN]) {
@@ -500,7 +507,8 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         }
     };
     if (kReadout) lds_row(kbeg, Cv);
-    Prelude cur = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
+    Prelude pp[kDB ? 2 : 1];
+    pp[0] = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
     ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[1 % P] : trow(kbeg + 1)) * (kN * 4), Bn);
     {
         uint32_t so;
@@ -514,9 +522,12 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         dr[0] = ld_raw(IO{}, rd, vo, so);
     }
 
-    auto body = [&](int kk, int j) {
+    auto body = [&](int kk, int j, int par) {  // step kk, ring slot j = (kk - kbeg) % P, parity (kk - kbeg) & 1
         const int jn = (j + 1) % P;
         const int tl = lt(kk);
+        Prelude& cur = pp[kDB ? par : 0];
+        Prelude nxt_copy;                              // without kDB: the next prelude, copied at the end
+        Prelude& nxt = kDB ? pp[par ^ 1] : nxt_copy;
         float Cn[kN];  // next token's C row, read from LDS a step ahead of its use
         if (kReadout) lds_row(kk + 1, Cn);
         // Consume the ring slots before refilling them: the empty asm takes the widened values
@@ -554,7 +565,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             if (kMode == kFinish && kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
         // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
-        const Prelude nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
+        nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
         ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[(j + 2) % P] : trow(kk + 2)) * (kN * 4), Bn);
         if (kMode == kAggregate) dsum += cur.delta2;
         float yv = ln.template update<kReadout>(cur, Cv);
@@ -579,7 +590,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         if (kMode == kOut)
             st_buf(IO{}, ry, vo, kOrd ? tokoff(ytok) : static_cast<uint32_t>(tl) * rowb,
                    silu(zv) * (kConv ? yv : fmaf(ln.Dd, cur.x, yv)));
-        cur = nxt;
+        if (!kDB) cur = nxt_copy;
         if (kReadout) {
 #pragma unroll
             for (int n = 0; n < kN; ++n) Cv[n] = Cn[n];
@@ -590,14 +601,15 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    constexpr int U = (kDB && P % 2) ? 2 * P : P;  // steps per loop iteration: a multiple of the ring depth (and of 2 with kDB)
     int k = kbeg;
-    for (; k + P <= kend; k += P) {
+    for (; k + U <= kend; k += U) {
 #pragma unroll
-        for (int j = 0; j < P; ++j) body(k + j, j);
+        for (int j = 0; j < U; ++j) body(k + j, j % P, j & 1);
     }
 #pragma unroll
-    for (int j = 0; j < P - 1; ++j)
-        if (k + j < kend) body(k + j, j);
+    for (int j = 0; j < U - 1; ++j)
+        if (k + j < kend) body(k + j, j % P, j & 1);
 }
 
 // The walk instance for this wave's transition form (wave-uniform).
