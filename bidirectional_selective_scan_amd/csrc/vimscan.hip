@@ -815,13 +815,15 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
 // scan order; carry[chunk] is replaced by the state entering that chunk. The fold is the
 // associative operator of the linear recurrence: (P1, e1) then (P2, e2) -> (P1 P2, P2 e1 + e2),
 // with P = exp(A * sum delta) the chunk's transition product.
-// Block: 256 threads = 64 channels x 4 states; grid (channel blocks, 4, 2 * nseq), or nseq in z
-// forward only.
+// Block: 256 threads = 64 channels x 4 states; grid (channel blocks x directions x sequences, 4)
+// with the channel block fastest in x (x holds the large count: y and z are limited to 65535).
 __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
-    const int d = static_cast<int>(blockIdx.x) * kWave + (static_cast<int>(threadIdx.x) & (kWave - 1));
+    const int bx = static_cast<int>(blockIdx.x);
+    const int zz = bx / a.ncb;  // direction + 2 * sequence, or the sequence forward only
+    const int d = (bx % a.ncb) * kWave + (static_cast<int>(threadIdx.x) & (kWave - 1));
     const int n = static_cast<int>(blockIdx.y) * 4 + (static_cast<int>(threadIdx.x) >> 6);
-    const int dir = a.uni ? 0 : static_cast<int>(blockIdx.z) & 1;
-    const int seq = a.uni ? static_cast<int>(blockIdx.z) : static_cast<int>(blockIdx.z) >> 1;
+    const int dir = a.uni ? 0 : zz & 1;
+    const int seq = a.uni ? zz : zz >> 1;
     if (d >= a.Di) return;
     const float an = a.A[dir][d * kN + n];
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
@@ -838,15 +840,17 @@ __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
 }
 
 // Auxiliary-token swap after the scan (VIMSCAN_FLAG_AUX_SWAP): exchange the first and the last
-// row of y in every sequence (segment). One thread per (sequence, channel); grid (channel groups
-// of 256, sequences).
+// row of y in every sequence (segment). One thread per (sequence, channel); a 1-D grid of
+// (channel group of 256) x sequences, channel group fastest.
 template <typename IO>
 __global__ __launch_bounds__(256) void k_aux_swap(ScanArgs a) {
     using E = typename IoTraits<IO>::elem;
-    const int d = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+    const int groups = (a.Di + 255) / 256;
+    const int seq = static_cast<int>(blockIdx.x) / groups;
+    const int d = (static_cast<int>(blockIdx.x) % groups) * 256 + static_cast<int>(threadIdx.x);
     if (d >= a.Di || a.Lp < 2) return;
     E* y = static_cast<E*>(a.y);
-    const int64_t first = static_cast<int64_t>(blockIdx.y) * a.Lp * a.Di + d;
+    const int64_t first = static_cast<int64_t>(seq) * a.Lp * a.Di + d;
     const int64_t last = first + static_cast<int64_t>(a.Lp - 1) * a.Di;
     const E v0 = y[first];
     y[first] = y[last];
@@ -999,7 +1003,7 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
     if (p.K > 1) {
         hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), 0,
                            s, a);
-        const dim3 cgrid(static_cast<unsigned>(p.ncb), 4, static_cast<unsigned>((p.uni ? 1 : 2) * p.nseq));
+        const dim3 cgrid(static_cast<unsigned>(p.ncb * (p.uni ? 1 : 2) * p.nseq), 4);
         hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
     const bool timed = ev0 != nullptr && ev1 != nullptr;
@@ -1018,7 +1022,7 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
     if (hipGetLastError() != hipSuccess) return VIMSCAN_ERR_HIP;
     if (timed && hipEventRecord(ev1, s) != hipSuccess) return VIMSCAN_ERR_HIP;
     if (p.swap) {
-        const dim3 sgrid(static_cast<unsigned>((a.Di + 255) / 256), static_cast<unsigned>(p.nseq));
+        const dim3 sgrid(static_cast<unsigned>((a.Di + 255) / 256 * p.nseq));
         hipLaunchKernelGGL(k_aux_swap<IO>, sgrid, dim3(256), 0, s, a);
         if (hipGetLastError() != hipSuccess) return VIMSCAN_ERR_HIP;
     }

@@ -213,3 +213,23 @@ def test_long_and_wide_extremes(B, L, Di, params, io):
     info = binding.launch_info(B, L, Di, 16, 0, io)
     y = to_f64(run_gpu(dev))
     assert_close(y, oracle.bidir_fwd(inp, nthreads=16), io, f"B={B} L={L} Di={Di} {params} plan={info}")
+
+
+def _swap_first_last(y, T):
+    out = y.copy()
+    for s0 in range(0, y.shape[1], T):
+        out[:, s0], out[:, s0 + T - 1] = y[:, s0 + T - 1], y[:, s0]
+    return out
+
+
+def test_many_folded_sequences_chunked_with_swap():
+    """70,000 folded sequences of 2 tokens, each cut into 2 chunks: the chunk-carry combine and the
+    auxiliary swap run over more sequences than a grid's y or z dimension may hold."""
+    T, nseq, Di = 2, 70000, 32
+    inp = _case(1, T * nseq, Di, "f32", seed=77, params="random")
+    dev = to_device(inp, "f32")
+    info = binding.launch_info(1, T * nseq, Di, 16, T, "f32", chunk_len=1)
+    assert info["chunks"] == 2 and info["sequences"] == nseq
+    y = to_f64(run_gpu(dev, seg_len=T, chunk_len=1, aux_swap=True))
+    ref = _swap_first_last(oracle.bidir_fwd(inp, seg_len=T, nthreads=16), T)
+    assert_close(y, ref, "f32", "many folded sequences")
