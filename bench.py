@@ -109,6 +109,7 @@ def cpu_baseline(inp: dict, w) -> dict:
     cores = oracle.max_threads()
     return {"value": round(w.algorithmic_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "seconds": round(t, 4), "cpu": cpu_model(),
+            "tokens_channels_per_s": round(w.tokens_channels / t, 1),
             "sample": f"the full {w.name} batch in float64 on {cores} OpenMP threads, median of 3 runs "
                       f"({round(3 * t * cores, 1)} core-seconds in all)"}
 
@@ -150,6 +151,9 @@ def main(argv=None):
     ap.add_argument("--no-ncssd", action="store_true", help="skip the NC-SSD global-state form measurement")
     ap.add_argument("--no-order", action="store_true",
                     help="skip the scan in a given token order (7 x 7 local windows of the patch grid)")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the scan on one GPU's share of an 8-way batch split (batch / 8)")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device-copy bandwidth ceiling")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the headline steps as eager library calls instead of HIP graph replays")
     ap.add_argument("--only-ncssd", action="store_true",
@@ -391,6 +395,42 @@ def main(argv=None):
                           "alu_frac": round(ops / ko / 1e12 / VALU_PEAK_TOPS, 4)}
     if not args.no_ncssd:
         out["ncssd"] = ncssd_leg(w, timed, stats_us, calls["ncssd"][0].plan, nc_bytes, nc_copies)
+    if not args.no_copy:
+        # measured HBM ceiling: a device copy of 512 MiB (read + write 1 GiB), outside the Infinity Cache
+        n = 512 * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ceil_gbs = 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        out["roofline"]["hbm"]["copy_ceiling"] = round(ceil_gbs, 1)
+        out["roofline"]["hbm"]["frac_of_copy"] = round(nbytes / kernel_s / 1e9 / ceil_gbs, 4)
+        if "ncssd" in out:
+            out["ncssd"]["roofline"]["copy_ceiling"] = round(ceil_gbs, 1)
+            out["ncssd"]["roofline"]["frac_of_copy"] = round(out["ncssd"]["roofline"]["achieved"] / ceil_gbs, 4)
+    if not args.no_shard and w.batch % 8 == 0 and w.batch >= 8:
+        # one GPU's share of an 8-way data-parallel split: the first batch / 8 rows of the same inputs
+        bs = w.batch // 8
+        sh = [[t[:bs] for t in copies[i]] for i in range(ncopy)]
+        plan_s = binding.launch_info(bs, w.seqlen, w.d_inner, 16, w.seg_len, w.io_dtype)
+        ws_s = torch.empty(max(plan_s["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+        calls["shard"] = [binding.PreparedCall(*sh[i], *params, seg_len=w.seg_len, out=outs[i][:bs], workspace=ws_s)
+                          for i in range(ncopy)]
+        wall_s, per_call_s, per_scan_s = timed("shard")
+        ks = float(np.mean(per_scan_s))
+        sbytes = (nbytes - (2 * w.d_inner * 16 + 4 * w.d_inner) * 4) // 8 + (2 * w.d_inner * 16 + 4 * w.d_inner) * 4
+        out["shard_1_of_8"] = {"what": f"the scan on one GPU's share of an 8-way batch split (batch {bs})",
+                               "value": round(sbytes * args.steps / wall_s / 1e9, 2), "unit": "GB/s",
+                               "call_us": stats_us(per_call_s), "kernel_us": round(ks * 1e6, 3),
+                               "alu_frac": round(ops / 8 / ks / 1e12 / VALU_PEAK_TOPS, 4),
+                               "plan": {k: plan_s[k] for k in ("chunks", "workgroups", "park_in_workspace")}}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out), flush=True)
