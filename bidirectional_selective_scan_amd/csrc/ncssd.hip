@@ -5,8 +5,10 @@
 // weights m_j (the reciprocal of the token's scalar transition),
 //     H = B^T (X . m)   [N x Di]   one hidden state shared by every token of the sequence
 //     Y = C H           [T x Di]   every token reads it out with its own C row
-// where X . m scales token j's row of X by m_j. Both are dense contractions with a short inner
-// (state) or outer (state) dimension, so they run on the matrix cores.
+// where X . m scales token j's row of X by m_j. Both are dense contractions (the first reduces
+// over the tokens into N states, the second over the N states), so they run on the matrix cores;
+// with N = 16 they move 16 flops per byte, far below the matrix cores' ridge point, so HBM bounds
+// the call and the design aims at reading x once and writing y once.
 //
 // Execution design (gfx950, wave64, MFMA 16x16 tiles):
 //  * A workgroup owns one sequence and 64 channels (k_ncssd_fused): its four waves take the
@@ -16,8 +18,8 @@
 //    split instead: pass 1 (k_ncssd_state) stores one partial state per token range, a small
 //    kernel (k_ncssd_reduce) adds them in range order into H in the workspace, and pass 2
 //    (k_ncssd_out) reads it out for groups of kOutTokens tokens. Results never depend on timing.
-//  * The state contraction of a wave, per 16-token tile: H += B'^T X with B' = B . m as the MFMA A operand
-//    (rows = states, K = tokens) and X as the B operand (K = tokens, columns =
+//  * The state contraction of a wave, per 16-token tile: H += B'^T X with B' = B . m as the MFMA
+//    A operand (rows = states, K = tokens) and X as the B operand (K = tokens, columns =
 //    channels). Each lane reads its four consecutive channels of four consecutive tokens as
 //    plain 8-byte (bf16) or 16-byte (fp32) row loads, so X needs no transposition through LDS:
 //    the four MFMA column sets of a wave are the channels d0 + 4c + q, q = 0..3, and the lane
@@ -35,6 +37,10 @@
 //    fp32 io uses the fp32 MFMA (16x16x4) directly.
 //  * Sequences are split only when sequences x channel blocks is below about a thousand
 //    workgroups, so the chip has several thousand waves either way.
+//  * Every load is unconditional at a row clamped into range (a token past a range is zeroed by a
+//    select where it would enter a sum), so a tile's loads are all in flight together; workgroup
+//    ids are remapped so the channel blocks of one sequence share an XCD's L2 (B, C and m are
+//    fetched from memory once).
 
 #include <hip/hip_runtime.h>
 
