@@ -793,6 +793,10 @@ template <typename IO, int kVar>
 __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     constexpr bool kConv = kVar == kWithConv;
     const WgCoords c = wg_coords(a, a.uni != 0);
+    // The state after the last chunk in scan order (forward: the last chunk, backward: the first)
+    // is never used, so that chunk's aggregate is not computed (no barrier follows: the wave may
+    // leave).
+    if (c.chunk == (c.dir == 0 ? a.K - 1 : 0)) return;
     Lane ln;
     ln.init(a, c.dir, c.dc, false);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
@@ -827,15 +831,30 @@ __global__ __launch_bounds__(256) void k_carry_combine(ScanArgs a) {
     if (d >= a.Di) return;
     const float an = a.A[dir][d * kN + n];
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
+    // Aggregates are read kB chunks at a time before any store (stores into the same workspace
+    // would otherwise order every load after the previous store: one memory round trip per chunk).
+    // The last chunk in scan order has no aggregate (its end state is never used): loads past the
+    // second-to-last chunk are clamped to it, and the value is not used.
+    constexpr int kB = 16;
     float H = 0.0f;
-    for (int k = 0; k < a.K; ++k) {
-        const int ch = dir == 0 ? k : a.K - 1 - k;
-        const int64_t slot = base + ch;
-        float* e = a.carry + (slot * kN + n) * a.Di + d;
-        const float s = a.dsum[slot * a.Di + d];
-        const float end = *e;
-        *e = H;
-        H = fmaf(fast_exp2(an * s), H, end);
+    for (int k0 = 0; k0 < a.K; k0 += kB) {
+        float ev[kB], sv[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int k = min(k0 + j, a.K - 2);  // K >= 2 when the combine runs
+            const int64_t slot = base + (dir == 0 ? k : a.K - 1 - k);
+            ev[j] = a.carry[(slot * kN + n) * a.Di + d];
+            sv[j] = a.dsum[slot * a.Di + d];
+        }
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+            const int k = k0 + j;
+            if (k < a.K) {
+                const int64_t slot = base + (dir == 0 ? k : a.K - 1 - k);
+                a.carry[(slot * kN + n) * a.Di + d] = H;  // the state entering chunk k
+                H = fmaf(fast_exp2(an * sv[j]), H, ev[j]);
+            }
+        }
     }
 }
 
