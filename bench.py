@@ -59,14 +59,17 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks,
 #   u*B[n]: 16 multiplies; state h = h*e + u*B: 16 FMAs; readout C.h: 16 FMAs + 1 add
 # Combine: yf + yb, + (D_f + D_b)*x, silu (-z*log2e, exp2, +1, rcp, *z), product
 #                                                                   6 ops + 2 transcendentals
+# Forward scan alone: one direction, then + D*x, silu, product      5 ops + 2 transcendentals
 TRANS_OPS = 2
 
 
-def alu_ops_per_element(geometric: bool) -> float:
+def alu_ops_per_element(geometric: bool, directions: int = 2) -> float:
+    """Lane-operations per (b, t, d) of the bidirectional path, or of the forward scan alone
+    (directions=1: no yf + yb add, so the gate stage is 5 ops + 2 transcendentals)."""
     per_dir_ops = 4 + 1 + 16 + 16 + 16 + 17
     per_dir_trans = 2 + (1 if geometric else 16)
-    ops = 2 * per_dir_ops + 6
-    trans = 2 * per_dir_trans + 2
+    ops = directions * per_dir_ops + (6 if directions == 2 else 5)
+    trans = directions * per_dir_trans + 2
     return ops + TRANS_OPS * trans
 
 
@@ -378,12 +381,17 @@ def main(argv=None):
         e_io = 2 if w.io_dtype == "bf16" else 4
         fbytes = (w.tokens_channels * 4 * e_io + 2 * w.batch * w.seqlen * 16 * e_io
                   + (w.d_inner * 16 + 2 * w.d_inner) * 4)
+        ops_f = alu_ops_per_element(geometric, directions=1) * w.tokens_channels
         for name, label in (("fwd", "forward_only"), ("fwd_swap", "forward_only_aux_swap")):
             wall_f, per_call_f, per_scan_f = timed(name)
+            kf = float(np.mean(per_scan_f))
             out[label] = {"what": "forward scan alone (vimscan_fwd)" + (", with the auxiliary-token swap"
                                                                          if name == "fwd_swap" else ""),
                           "value": round(fbytes * args.steps / wall_f / 1e9, 2), "unit": "GB/s",
-                          "call_us": stats_us(per_call_f), "kernel_us": round(float(np.mean(per_scan_f)) * 1e6, 3)}
+                          "call_us": stats_us(per_call_f), "kernel_us": round(kf * 1e6, 3),
+                          "alu_achieved_tops": round(ops_f / kf / 1e12, 3),
+                          "alu_frac": round(ops_f / kf / 1e12 / VALU_PEAK_TOPS, 4),
+                          "ops_per_element": alu_ops_per_element(geometric, directions=1)}
     if not args.no_order:
         wall_o, per_call_o, per_scan_o = timed("order")
         ko = float(np.mean(per_scan_o))
