@@ -4,7 +4,7 @@ One step = one call of the whole path (forward scan, backward scan, gate) over o
 Vim-S workload (batch 128, 197 tokens, d_inner 768, N 16, bf16 I/O, fp32 state). Prints one JSON
 line. ``value`` is GB/s of algorithmic traffic (read x, dt, z, B_f, C_f, B_b, C_b and the fp32
 parameters once, write y once) over the K timed steps. The timed steps are replays of HIP graphs
-holding one whole library call (the B-row widening and the scan kernel) per input copy, so host
+holding one whole library call (the scan kernel, with the chunk passes when the plan has them) per input copy, so host
 launch work is off the critical path (``--no-graph`` times eager calls instead); the per-kernel times
 come from an eager pass in which the library records its events around the scan kernel. The steps rotate over several copies of the
 inputs (more than the 256 MB Infinity Cache holds), so every step reads its inputs from HBM.
@@ -284,9 +284,8 @@ def main(argv=None):
     kernel_s = float(np.mean(per_scan))
     launch_mode = "eager library calls"
     if not args.no_graph:
-        # The headline steps: one HIP graph per input copy holding the whole call (the B-row
-        # widening and the scan kernel), captured once and replayed, so the host's per-call
-        # launch work is not on the GPU's critical path.
+        # The headline steps: one HIP graph per input copy holding the whole call, captured once
+        # and replayed, so the host's per-call launch work is not on the GPU's critical path.
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):

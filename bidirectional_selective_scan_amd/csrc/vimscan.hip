@@ -13,11 +13,11 @@
 //    B sequences of T tokens, so the kernels index segments as sequences. No copy, no select.
 //  * One workgroup = one chunk of one sequence x 64 channels, two waves: wave 0 runs the forward
 //    recurrence, wave 1 the backward one, one channel per lane, the 16 states in VGPRs. A token's
-//    B and C rows are the same for every channel of a sequence, so they are wave-uniform: fp32
-//    B rows come through the scalar unit into SGPRs (bf16 rows are first widened to fp32 by a
-//    small pre-pass, so the loop spends no scalar instructions unpacking them); C rows are
-//    staged once per workgroup in LDS and read as broadcasts (a wave-uniform vector load would
-//    return the same 64 bytes to every lane through the vector memory path).
+//    B and C rows are the same for every channel of a sequence, so they are wave-uniform: the
+//    chunk's B and C rows of both directions are staged once per workgroup in LDS as fp32
+//    (bf16 widened on the way) and read as broadcasts. Nothing in the token loop goes through
+//    the scalar memory path: scalar loads complete out of order, so a wait for any of them is a
+//    wait for all, which left only one token of latency hiding for a row fetched from HBM.
 //  * The two directions meet in the middle of the chunk: in the first half each wave parks its
 //    branch output (forward for the first half of the chunk, backward for the second), then
 //    after one barrier each wave finishes its own half, adds the parked output of the other
@@ -45,8 +45,8 @@
 //  * Variants of the same kernels (a template parameter): the directional convolution in front
 //    of each direction (a register window of the previous raw inputs in walk order), and the scan
 //    in a given token order (a step's token is looked up in the order through the scalar unit;
-//    chunks are ranges of steps, C rows are gathered into LDS in step order, so the park, the
-//    meeting point and the chunk carries stay indexed by step).
+//    chunks are ranges of steps, B and C rows are gathered into LDS in step order, so the park,
+//    the meeting point and the chunk carries stay indexed by step).
 
 #include <hip/hip_runtime.h>
 
@@ -135,24 +135,12 @@ __device__ __forceinline__ void st_buf(Bf16, __amdgpu_buffer_rsrc_t r, uint32_t 
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, b), r, vo, so, 0);
 }
 
-// One token's fp32 B or C row (16 values), read through the scalar unit: the row address is
-// wave-uniform and the constant address space makes the compiler emit scalar loads.
-// The row is given as a base and a 32-bit byte offset, which the scalar load takes as its
-// offset operand (no 64-bit address arithmetic per row).
-typedef const float __attribute__((address_space(4)))* ConstRow;
-__device__ __forceinline__ void ld_row(const float* base, uint32_t off, float (&v)[kN]) {
-    const ConstRow p = (ConstRow)(reinterpret_cast<const char*>(base) + off);
-#pragma unroll
-    for (int n = 0; n < kN; ++n) v[n] = p[n];
-}
-
 struct ScanArgs {
     const void* x;
     const void* dt;
     const void* z;
     const void* Bm[2];      // io-dtype rows as passed: [0] forward, [1] backward
     const void* Cm[2];
-    const float* Brow[2];   // fp32 B rows the scan reads (the inputs, or their widened copies)
     const float* A[2];
     const float* D[2];
     const float* dtb[2];
@@ -160,8 +148,6 @@ struct ScanArgs {
     float* carry;  // chunked: [dir][seq][chunk][n][Di] states (x log2 e); pass 1 end states / pass 2 inputs
     float* dsum;   // chunked: [dir][seq][chunk][Di] sum of delta * log2(e) over the chunk
     float* parkg;  // park in global memory: [workgroup][T][64] (null: the park is in LDS)
-    float* rows;   // bf16 io: widened B rows [B_f, B_b][tokens][16]
-    int64_t tokens;  // batch * seqlen
     int Lp;        // tokens per independent sequence
     int Di;
     int nseq;
@@ -378,7 +364,8 @@ __device__ __forceinline__ uint32_t ld_global_raw(const void* base, int64_t i) {
 // outside the sequence).
 template <typename IO, int kDecay, int kMode, bool kGlobalPark, int kVar>
 __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
-                                     const float* lds_c, int kbeg, int kend, float& dsum) {
+                                     const float* lds_c, const float* lds_b, const int32_t* lds_ord, int kbeg,
+                                     int kend, float& dsum) {
     constexpr bool kConv = kVar == kWithConv;
     constexpr bool kOrd = kVar == kOrdered;
     constexpr int P = kConv ? 3 : 4;  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
@@ -403,7 +390,6 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const __amdgpu_buffer_rsrc_t rp =
         chunk_rsrc(kGlobalPark ? a.parkg + static_cast<int64_t>(c.slot) * a.T * kWave : nullptr,
                    static_cast<uint32_t>(a.T) * kWave * 4);
-    const float* Bs = uniform_ptr(a.Brow[c.dir] + rbase * kN);
     const uint32_t vo = static_cast<uint32_t>(c.dc) * e;
     const uint32_t vp = static_cast<uint32_t>(c.lane) * 4;
     const int last = kend - 1;
@@ -414,20 +400,13 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     const int tbase = c.dir * (len - 1);
     auto lt = [&](int k) { return tbase + sgn * k; };
     // Token row (from rbase) of walk step min(k, last): the step itself, or in a given order the
-    // token the order lists for it, read through the scalar unit and clamped into the sequence
-    // (an order that is not a permutation gives unspecified outputs but no access outside it).
-    // The order entry is read with a 32-bit byte offset, which the scalar load takes as its offset
-    // operand (no 64-bit address arithmetic per step).
-    typedef const int32_t __attribute__((address_space(4)))* OrdPtr;
-    const char* ordb = reinterpret_cast<const char*>(uniform_ptr(kOrd ? a.order + row0 : a.order));
+    // token the order lists for it, read from the chunk's copy of the order in LDS (a broadcast
+    // read; no scalar load in the loop) and clamped into the sequence (an order that is not a
+    // permutation gives unspecified outputs but no access outside it).
     auto trow = [&](int k) -> int {
         const int st = lt(min(k, last));
-        if constexpr (kOrd) {
-            const OrdPtr p = (OrdPtr)(ordb + static_cast<uint32_t>(st) * 4u);
-            return min(max(static_cast<int>(*p), 0), a.Lp - 1);
-        } else {
-            return st;
-        }
+        if constexpr (kOrd) return min(max(lds_ord[st], 0), a.Lp - 1);
+        else return st;
     };
     auto toff = [&](int k) {  // token row byte offset of walk step min(k, last)
         return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(trow(k))) * rowb;
@@ -483,20 +462,13 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
                                                       : 0u;
         }
     }
-    // B rows (SGPRs) run one token ahead: B(k+1) is consumed by the prelude of token k+1 during
-    // step k. C rows come from the chunk's copy in LDS (staged once per workgroup), read as
-    // wave-uniform broadcasts at the start of the step that uses them.
-    // The current and the next token's prelude live in two buffers used alternately by the parity
-    // of the walk step (a compile-time index in the unrolled loop), so the 34 values are not copied
-    // from "next" to "current" between tokens (the register allocator could not line the copies up
-    // with the loop-carried registers). Only the plain bf16 instances do this: the convolution and
-    // ordered variants have no registers for a second prelude at 3 waves per SIMD (168 VGPRs), and
-    // the fp32 instances measured no faster (slower with general transitions).
-    constexpr bool kDB = kVar == kPlain && IoTraits<IO>::bytes == 2;
+    // B and C rows come from the chunk's copy in LDS (staged once per workgroup), read as
+    // wave-uniform broadcasts at the start of the step that uses them: during step k the C row of
+    // token k (its readout) and the B row of token k+1 (its prelude). Nothing is held across a
+    // token boundary but the state, the next token's prelude and the register rings.
     float Bn[kN], Cv[kN];
-    ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[0] : trow(kbeg)) * (kN * 4), Bn);
-    auto lds_row = [&](int k, float (&v)[kN]) {
-        const float4* cp = reinterpret_cast<const float4*>(lds_c + lt(min(k, last)) * kN);
+    auto lds_row = [&](const float* rows, int k, float (&v)[kN]) {  // the row of walk step min(k, last)
+        const float4* cp = reinterpret_cast<const float4*>(rows + lt(min(k, last)) * kN);
 #pragma unroll
         for (int q = 0; q < kN / 4; ++q) {
             const float4 f = cp[q];
@@ -506,10 +478,8 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             v[4 * q + 3] = f.w;
         }
     };
-    if (kReadout) lds_row(kbeg, Cv);
-    Prelude pp[kDB ? 2 : 1];
-    pp[0] = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
-    ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[1 % P] : trow(kbeg + 1)) * (kN * 4), Bn);
+    lds_row(lds_b, kbeg, Bn);
+    Prelude cur = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
     {
         uint32_t so;
         if constexpr (kOrd) {
@@ -522,14 +492,11 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         dr[0] = ld_raw(IO{}, rd, vo, so);
     }
 
-    auto body = [&](int kk, int j, int par) {  // step kk, ring slot j = (kk - kbeg) % P, parity (kk - kbeg) & 1
+    auto body = [&](int kk, int j) {  // step kk, ring slot j = (kk - kbeg) % P
         const int jn = (j + 1) % P;
         const int tl = lt(kk);
-        Prelude& cur = pp[kDB ? par : 0];
-        Prelude nxt_copy;                              // without kDB: the next prelude, copied at the end
-        Prelude& nxt = kDB ? pp[par ^ 1] : nxt_copy;
-        float Cn[kN];  // next token's C row, read from LDS a step ahead of its use
-        if (kReadout) lds_row(kk + 1, Cn);
+        if (kReadout) lds_row(lds_c, kk, Cv);  // this token's C row
+        lds_row(lds_b, kk + 1, Bn);  // next token's B row, for its prelude below
         // Consume the ring slots before refilling them: the empty asm takes the widened values
         // and orders every load after it, so a refill can reuse its slot's register and the loop
         // needs no register copies (a copy would wait for the load just issued).
@@ -564,9 +531,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             zr[j] = ld_raw(IO{}, rz, vo, so);
             if (kMode == kFinish && kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
-        // next token's prelude (uses B(k+1)), then request B(k+2) into the same SGPRs
-        nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
-        ld_row(Bs, static_cast<uint32_t>(kOrd ? tx[(j + 2) % P] : trow(kk + 2)) * (kN * 4), Bn);
+        const Prelude nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);  // next token's prelude
         if (kMode == kAggregate) dsum += cur.delta2;
         float yv = ln.template update<kReadout>(cur, Cv);
         if (kConv && kReadout) yv = fmaf(ln.Dd, cur.x, yv);  // own skip term on own input u
@@ -590,142 +555,131 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         if (kMode == kOut)
             st_buf(IO{}, ry, vo, kOrd ? tokoff(ytok) : static_cast<uint32_t>(tl) * rowb,
                    silu(zv) * (kConv ? yv : fmaf(ln.Dd, cur.x, yv)));
-        if (!kDB) cur = nxt_copy;
-        if (kReadout) {
-#pragma unroll
-            for (int n = 0; n < kN; ++n) Cv[n] = Cn[n];
-        }
+        cur = nxt;
         // Token boundary: no instruction moves across it. Within a token the next prelude and
         // this update interleave freely; across tokens the scheduler would hoist preludes ahead
         // of the loads they wait for.
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    constexpr int U = (kDB && P % 2) ? 2 * P : P;  // steps per loop iteration: a multiple of the ring depth (and of 2 with kDB)
+    constexpr int U = P;  // steps per loop iteration: the ring depth (ring slots are compile-time indices)
     int k = kbeg;
     for (; k + U <= kend; k += U) {
 #pragma unroll
-        for (int j = 0; j < U; ++j) body(k + j, j % P, j & 1);
+        for (int j = 0; j < U; ++j) body(k + j, j % P);
     }
 #pragma unroll
     for (int j = 0; j < U - 1; ++j)
-        if (k + j < kend) body(k + j, j % P, j & 1);
+        if (k + j < kend) body(k + j, j % P);
 }
 
 // The walk instance for this wave's transition form (wave-uniform).
 template <typename IO, int kMode, bool kGlobalPark, int kVar>
 __device__ __forceinline__ void walk_as(int form, const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
-                                        const float* lds_c, int kbeg, int kend, float& dsum) {
+                                        const float* lds_c, const float* lds_b, const int32_t* lds_ord, int kbeg,
+                                        int kend, float& dsum) {
     if (form == kGeometric)
-        walk<IO, kGeometric, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+        walk<IO, kGeometric, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend, dsum);
     else if (form == kProgression)
-        walk<IO, kProgression, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+        walk<IO, kProgression, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend, dsum);
     else
-        walk<IO, kGeneral, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, kbeg, kend, dsum);
+        walk<IO, kGeneral, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend, dsum);
 }
 
-// Widen the bf16 B rows to fp32 rows once per call: [B_f, B_b][tokens][16], read through the
-// scalar unit by the scan. One thread per 32-bit word (two bf16 values).
-__global__ __launch_bounds__(256) void k_widen_rows(ScanArgs a) {
-    const int64_t words = a.tokens * (kN / 2);
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= 2 * words) return;
-    const int which = static_cast<int>(i / words);  // 0 B_f, 1 B_b
-    const int64_t w = i - which * words;
-    const uint32_t u = static_cast<const uint32_t*>(a.Bm[which])[w];
-    float2 f;
-    f.x = __uint_as_float(u << 16);
-    f.y = __uint_as_float(u & 0xffff0000u);
-    reinterpret_cast<float2*>(a.rows + which * a.tokens * kN)[w] = f;
+// Copy the chunk's rows into LDS as fp32: regions [C forward, C backward, B forward, B backward]
+// of [T][16] each (forward only: [C, B]), C times ln 2 (the state is kept in log2 units), B as
+// given; with withC false only the B regions, from region 0. Every row a walk reads then comes
+// from LDS, so its waits never include a scalar load (those complete out of order, and a wait for
+// one waits for every scalar load in flight). Each (matrix, direction) is one contiguous range of
+// 32-bit words in memory; every thread issues all its loads before widening and storing, so the
+// copy costs one memory round trip.
+// Region reg of the staged rows (0 C forward, 1 C backward, 2 B forward, 3 B backward; forward
+// only: 0 C, 1 B), chosen with selects (no run-time index into the kernel arguments).
+__device__ __forceinline__ const void* region_rows(const ScanArgs& a, int reg, int ndir) {
+    if (ndir == 1) return reg == 0 ? a.Cm[0] : a.Bm[0];
+    return reg == 0 ? a.Cm[0] : reg == 1 ? a.Cm[1] : reg == 2 ? a.Bm[0] : a.Bm[1];
 }
 
-// The same when both B tensors are 16-byte aligned: one thread per 16 bytes (8 values), so the
-// pass moves the same bytes with a quarter of the threads.
-__global__ __launch_bounds__(256) void k_widen_rows16(ScanArgs a) {
-    const int64_t quads = a.tokens * (kN / 8);
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= (a.uni ? 1 : 2) * quads) return;
-    const int which = static_cast<int>(i / quads);  // 0 B_f, 1 B_b
-    const int64_t q = i - which * quads;
-    const uint4 u = static_cast<const uint4*>(a.Bm[which])[q];
-    float4 lo, hi;
-    lo.x = __uint_as_float(u.x << 16);
-    lo.y = __uint_as_float(u.x & 0xffff0000u);
-    lo.z = __uint_as_float(u.y << 16);
-    lo.w = __uint_as_float(u.y & 0xffff0000u);
-    hi.x = __uint_as_float(u.z << 16);
-    hi.y = __uint_as_float(u.z & 0xffff0000u);
-    hi.z = __uint_as_float(u.w << 16);
-    hi.w = __uint_as_float(u.w & 0xffff0000u);
-    float4* dst = reinterpret_cast<float4*>(a.rows + which * a.tokens * kN) + 2 * q;
-    dst[0] = lo;
-    dst[1] = hi;
-}
-
-// Copy the chunk's C rows of both directions into LDS as fp32 times ln 2 (the state is kept in
-// log2 units): lds_c[dir][t][16], t in [0, len).
-// Each direction's rows are one contiguous range of 32-bit words in memory; every thread issues
-// all its loads before widening and storing, so the copy costs one memory round trip.
 template <typename IO>
-__device__ __forceinline__ void stage_c_rows(const ScanArgs& a, const WgCoords& c, float* lds_c, bool uni) {
+__device__ __forceinline__ void stage_rows(const ScanArgs& a, const WgCoords& c, float* lds, bool uni, bool withC) {
     constexpr int kU = 16;                                     // words per thread per pass
     constexpr int kPerWord = 4 / IoTraits<IO>::bytes;          // values per 32-bit word
+    using El = typename IoTraits<IO>::elem;
     const int len = c.t1 - c.t0;
-    const int64_t row0 = static_cast<int64_t>(c.seq) * a.Lp + c.t0;
-    const int wpd = len * kN / kPerWord;                       // words per direction
-    const uint32_t* src0 = reinterpret_cast<const uint32_t*>(
-        static_cast<const typename IoTraits<IO>::elem*>(a.Cm[0]) + row0 * kN);
-    const uint32_t* src1 = reinterpret_cast<const uint32_t*>(
-        static_cast<const typename IoTraits<IO>::elem*>(a.Cm[1]) + row0 * kN);
-    const int nw = (uni ? 1 : 2) * wpd;                     // words to stage (forward only: one direction)
+    const int64_t off = (static_cast<int64_t>(c.seq) * a.Lp + c.t0) * kN;
+    const int wpd = len * kN / kPerWord;                       // words per (matrix, direction)
+    const int ndir = uni ? 1 : 2;
+    const int first = withC ? 0 : ndir;                        // first region: C forward, or B forward
+    const int nreg = 2 * ndir - first;                         // regions staged
+    const int nw = nreg * wpd;                                 // words to stage
+    const uint32_t* src[4];  // rows of regions first .. first + nreg - 1 in memory (uniform pointers)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        src[r] = reinterpret_cast<const uint32_t*>(static_cast<const El*>(region_rows(a, min(first + r, 2 * ndir - 1), ndir)) + off);
     const int nt = static_cast<int>(blockDim.x);
     for (int base = static_cast<int>(threadIdx.x); base < nw; base += kU * nt) {
         uint32_t w[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int i = base + u * nt;
-            w[u] = i < wpd ? src0[i] : (i < nw ? src1[i - wpd] : 0u);
+            const int r = min(i / wpd, nreg - 1);
+            const uint32_t* q = r == 0 ? src[0] : r == 1 ? src[1] : r == 2 ? src[2] : src[3];
+            w[u] = i < nw ? q[i - r * wpd] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int i = base + u * nt;
             if (i < nw) {
-                const int dir = i >= wpd ? 1 : 0;
-                float* dst = lds_c + dir * a.T * kN + (i - dir * wpd) * kPerWord;
+                const int r = i / wpd;
+                const float sc = first + r < ndir ? kLn2 : 1.0f;
+                float* dst = lds + r * a.T * kN + (i - r * wpd) * kPerWord;
                 if (kPerWord == 1) {
-                    dst[0] = __uint_as_float(w[u]) * kLn2;
+                    dst[0] = __uint_as_float(w[u]) * sc;
                 } else {
-                    dst[0] = __uint_as_float(w[u] << 16) * kLn2;
-                    dst[1] = __uint_as_float(w[u] & 0xffff0000u) * kLn2;
+                    dst[0] = __uint_as_float(w[u] << 16) * sc;
+                    dst[1] = __uint_as_float(w[u] & 0xffff0000u) * sc;
                 }
             }
         }
     }
 }
 
-// The same for a scan in a given order: the chunk's C rows are gathered in step order (row k of
-// direction dir in LDS is the C row of the token the order lists for step t0 + k), so the walk
-// reads them exactly as in raster order. One 32-bit word per thread and pass.
+// The same for a scan in a given order (both directions, C and B): the chunk's rows are gathered
+// in step order (row k of a region is the row of the token the order lists for step t0 + k), so
+// the walk reads them exactly as in raster order. One thread per (region, row): one lookup in the
+// order, then the row's words as independent loads, so a pass costs two dependent memory round
+// trips whatever the row's width.
 template <typename IO>
-__device__ __forceinline__ void stage_c_rows_ordered(const ScanArgs& a, const WgCoords& c, float* lds_c) {
+__device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCoords& c, float* lds, bool withC) {
     constexpr int kPerWord = 4 / IoTraits<IO>::bytes;
     constexpr int wpr = kN / kPerWord;  // words per row
+    using El = typename IoTraits<IO>::elem;
     const int len = c.t1 - c.t0;
     const int64_t srow = static_cast<int64_t>(c.seq) * a.Lp;
     const int32_t* ord = a.order + srow + c.t0;
-    const int nw = 2 * len * wpr;
-    for (int i = static_cast<int>(threadIdx.x); i < nw; i += static_cast<int>(blockDim.x)) {
-        const int dir = i / (len * wpr);
-        const int k = (i / wpr) % len, w = i % wpr;
+    const int first = withC ? 0 : 2;
+    const int nrows = (4 - first) * len;
+    int32_t* lds_ord = reinterpret_cast<int32_t*>(lds + (4 - first) * a.T * kN);  // after the rows
+    for (int i = static_cast<int>(threadIdx.x); i < len; i += static_cast<int>(blockDim.x)) lds_ord[i] = ord[i];
+    for (int i = static_cast<int>(threadIdx.x); i < nrows; i += static_cast<int>(blockDim.x)) {
+        const int r = i / len, k = i - r * len;  // region (from first) and step
+        const int reg = first + r;
         const int tok = min(max(static_cast<int>(ord[k]), 0), a.Lp - 1);
-        const uint32_t u = reinterpret_cast<const uint32_t*>(
-            static_cast<const typename IoTraits<IO>::elem*>(a.Cm[dir]) + (srow + tok) * kN)[w];
-        float* dst = lds_c + dir * a.T * kN + k * kN + w * kPerWord;
-        if (kPerWord == 1) {
-            dst[0] = __uint_as_float(u) * kLn2;
-        } else {
-            dst[0] = __uint_as_float(u << 16) * kLn2;
-            dst[1] = __uint_as_float(u & 0xffff0000u) * kLn2;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const El*>(region_rows(a, reg, 2)) +
+                                                                (srow + tok) * kN);
+        uint32_t w[wpr];
+#pragma unroll
+        for (int q = 0; q < wpr; ++q) w[q] = src[q];
+        const float sc = reg < 2 ? kLn2 : 1.0f;
+        float* dst = lds + r * a.T * kN + k * kN;
+#pragma unroll
+        for (int q = 0; q < wpr; ++q) {
+            if (kPerWord == 1) {
+                dst[q] = __uint_as_float(w[q]) * sc;
+            } else {
+                dst[2 * q] = __uint_as_float(w[q] << 16) * sc;
+                dst[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u) * sc;
+            }
         }
     }
 }
@@ -736,12 +690,16 @@ __device__ __forceinline__ void stage_c_rows_ordered(const ScanArgs& a, const Wg
 template <typename IO, bool kCarry, bool kGlobalPark, int kVar>
 __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     constexpr bool kConv = kVar == kWithConv;
-    extern __shared__ float lds[];  // C rows [2][T][16], then the park [subs][T][64] when in LDS
+    // LDS: C and B rows [4][T][16]; in a given order the chunk's order [T]; the park [subs][T][64]
+    // when in LDS
+    extern __shared__ float lds[];
     const WgCoords c = wg_coords(a, false);
-    float* lds_c = lds + c.dir * a.T * kN;
-    float* lds_park = lds + 2 * a.T * kN + c.sub * a.T * kWave;
-    if constexpr (kVar == kOrdered) stage_c_rows_ordered<IO>(a, c, lds);
-    else stage_c_rows<IO>(a, c, lds, false);
+    const float* lds_c = lds + c.dir * a.T * kN;
+    const float* lds_b = lds + (2 + c.dir) * a.T * kN;
+    const int32_t* lds_ord = reinterpret_cast<const int32_t*>(lds + 4 * a.T * kN);
+    float* lds_park = lds + 4 * a.T * kN + (kVar == kOrdered ? a.T : 0) + c.sub * a.T * kWave;
+    if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, true);
+    else stage_rows<IO>(a, c, lds, false, true);
     Lane ln;
     ln.init(a, c.dir, c.dc, kConv);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
@@ -758,19 +716,19 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     const int half = len >> 1;
     const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
     float unused = 0.0f;
-    __syncthreads();  // the C rows are staged
-    walk_as<IO, kPark, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, 0, n1, unused);
+    __syncthreads();  // the rows are staged
+    walk_as<IO, kPark, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, 0, n1, unused);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
-    walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, n1, len, unused);
+    walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, n1, len, unused);
 }
 
 // Forward-only scan (vimscan_fwd): one chunk of one sequence, every wave a channel block of 64,
 // all walking forward; each token is gated and stored at once (no park, no meeting point).
 template <typename IO, bool kCarry>
 __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
-    extern __shared__ float lds[];  // the chunk's C rows [T][16]
+    extern __shared__ float lds[];  // the chunk's C rows [T][16], then its B rows [T][16]
     const WgCoords c = wg_coords(a, true);
-    stage_c_rows<IO>(a, c, lds, true);
+    stage_rows<IO>(a, c, lds, true, true);
     Lane ln;
     ln.init(a, 0, c.dc, true);
     if (kCarry) {
@@ -783,8 +741,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
     }
     const int form = ln.decay_form(a, 0, c.dc);
     float unused = 0.0f;
-    __syncthreads();  // the C rows are staged
-    walk_as<IO, kOut, false, kPlain>(form, a, c, ln, nullptr, lds, 0, c.t1 - c.t0, unused);
+    __syncthreads();  // the rows are staged
+    walk_as<IO, kOut, false, kPlain>(form, a, c, ln, nullptr, lds, lds + a.T * kN, nullptr, 0, c.t1 - c.t0, unused);
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
@@ -792,7 +750,11 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
 template <typename IO, int kVar>
 __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     constexpr bool kConv = kVar == kWithConv;
+    extern __shared__ float lds[];  // the chunk's B rows [directions][T][16]; in a given order then the order [T]
     const WgCoords c = wg_coords(a, a.uni != 0);
+    if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, false);
+    else stage_rows<IO>(a, c, lds, a.uni != 0, false);
+    __syncthreads();  // the rows are staged
     // The state after the last chunk in scan order (forward: the last chunk, backward: the first)
     // is never used, so that chunk's aggregate is not computed (no barrier follows: the wave may
     // leave).
@@ -805,7 +767,8 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     const int form = ln.decay_form(a, c.dir, c.dc);
     const int len = c.t1 - c.t0;
     float s = 0.0f;
-    walk_as<IO, kAggregate, false, kVar>(form, a, c, ln, nullptr, nullptr, 0, len, s);
+    walk_as<IO, kAggregate, false, kVar>(form, a, c, ln, nullptr, nullptr, lds + c.dir * a.T * kN,
+                                         reinterpret_cast<const int32_t*>(lds + 2 * a.T * kN), 0, len, s);
     if (c.valid) {
         const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
         float* dst = a.carry + slot * kN * a.Di;
@@ -882,9 +845,9 @@ __global__ __launch_bounds__(256) void k_aux_swap(ScanArgs a) {
 struct Plan {
     int64_t nseq, Lp, T, K, ncb, subs, wgs;
     int kernels;
-    bool park_global, widen, uni, swap;
+    bool park_global, uni, swap;
     size_t ws;                                 // total scratch bytes
-    size_t off_dsum, off_park, off_rows;      // byte offsets of the regions after the carries
+    size_t off_dsum, off_park;                // byte offsets of the regions after the carries
 };
 
 // A park larger than this goes to global scratch: in LDS it would cap a CU at fewer than 8
@@ -974,19 +937,16 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     if (p->uni) p->subs = p->ncb >= 4 ? 4 : p->ncb;
     else p->subs = p->ncb >= 2 ? 2 : 1;
     p->wgs = p->nseq * p->K * ((p->ncb + p->subs - 1) / p->subs);
-    p->widen = l->io_dtype == VIMSCAN_BF16;
-    p->kernels = (p->K > 1 ? 3 : 1) + (p->widen ? 1 : 0) + (p->swap ? 1 : 0);
+    p->kernels = (p->K > 1 ? 3 : 1) + (p->swap ? 1 : 0);
     p->park_global = !p->uni && p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
     const size_t f = sizeof(float);
     const size_t ndir = p->uni ? 1 : 2;
     const size_t carry = p->K > 1 ? static_cast<size_t>(ndir * p->nseq * p->K) * kN * l->d_inner * f : 0;
     const size_t dsum = p->K > 1 ? static_cast<size_t>(ndir * p->nseq * p->K) * l->d_inner * f : 0;
     const size_t park = p->park_global ? static_cast<size_t>(p->wgs) * p->subs * p->T * kWave * f : 0;
-    const size_t rows = p->widen ? ndir * l->batch * l->seqlen * kN * f : 0;
     p->off_dsum = round_up(carry, 256);
     p->off_park = round_up(p->off_dsum + dsum, 256);
-    p->off_rows = round_up(p->off_park + park, 256);
-    p->ws = (carry + dsum + park + rows) > 0 ? p->off_rows + rows : 0;
+    p->ws = (carry + dsum + park) > 0 ? p->off_park + park : 0;
     return VIMSCAN_OK;
 }
 
@@ -1003,32 +963,25 @@ unsigned wg_threads(const Plan& p) { return static_cast<unsigned>((p.uni ? 64 : 
 template <typename IO, bool kGlobalPark, int kVar>
 void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
     const dim3 grid(static_cast<unsigned>(p.wgs)), block(wg_threads(p));
-    const size_t lds = (2 * p.T * kN + (kGlobalPark ? 0 : p.subs * p.T * kWave)) * sizeof(float);
+    const size_t lds =
+        (4 * p.T * kN + (kVar == kOrdered ? p.T : 0) + (kGlobalPark ? 0 : p.subs * p.T * kWave)) * sizeof(float);
     if (carry) hipLaunchKernelGGL((k_bidir_scan<IO, true, kGlobalPark, kVar>), grid, block, lds, s, a);
     else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark, kVar>), grid, block, lds, s, a);
 }
 
 template <typename IO, int kVar>
 int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (p.widen) {
-        if (aligned(a.Bm[0], 16) && aligned(a.Bm[1], 16)) {
-            const int64_t threads = a.tokens * (kN / 8) * (p.uni ? 1 : 2);
-            hipLaunchKernelGGL(k_widen_rows16, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
-        } else {
-            const int64_t threads = a.tokens * (kN / 2) * (p.uni ? 1 : 2);
-            hipLaunchKernelGGL(k_widen_rows, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s, a);
-        }
-    }
     if (p.K > 1) {
-        hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), 0,
-                           s, a);
+        const size_t lds = (static_cast<size_t>(p.uni ? 1 : 2) * p.T * kN + (kVar == kOrdered ? p.T : 0)) * sizeof(float);
+        hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
+                           lds, s, a);
         const dim3 cgrid(static_cast<unsigned>(p.ncb * (p.uni ? 1 : 2) * p.nseq), 4);
         hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
     const bool timed = ev0 != nullptr && ev1 != nullptr;
     if (timed && hipEventRecord(ev0, s) != hipSuccess) return VIMSCAN_ERR_HIP;
     if (p.uni) {
-        const size_t lds = static_cast<size_t>(p.T) * kN * sizeof(float);
+        const size_t lds = 2 * static_cast<size_t>(p.T) * kN * sizeof(float);
         if (p.K > 1) hipLaunchKernelGGL((k_fwd_scan<IO, true>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
                                         lds, s, a);
         else hipLaunchKernelGGL((k_fwd_scan<IO, false>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), lds,
@@ -1128,15 +1081,6 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.carry = p.K > 1 ? reinterpret_cast<float*>(ws) : nullptr;
     a.dsum = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_dsum) : nullptr;
     a.parkg = p.park_global ? reinterpret_cast<float*>(ws + p.off_park) : nullptr;
-    a.rows = p.widen ? reinterpret_cast<float*>(ws + p.off_rows) : nullptr;
-    a.tokens = launch->batch * launch->seqlen;
-    if (p.widen) {
-        a.Brow[0] = a.rows;
-        a.Brow[1] = a.rows + a.tokens * kN;
-    } else {
-        a.Brow[0] = static_cast<const float*>(B_f);
-        a.Brow[1] = static_cast<const float*>(B_b);
-    }
     a.Lp = static_cast<int>(p.Lp);
     a.Di = static_cast<int>(launch->d_inner);
     a.nseq = static_cast<int>(p.nseq);

@@ -135,19 +135,16 @@ typedef struct vimscan_plan {
     int64_t sequences;      /* independent sequences: batch, or batch*seqlen/seg_len */
     int64_t seq_tokens;     /* tokens per independent sequence */
     int64_t chunk_len;      /* tokens per chunk */
-    int64_t chunks;         /* chunks per sequence; 1 = single pass, no workspace */
+    int64_t chunks;         /* chunks per sequence; 1 = single pass (no chunk carries) */
     int64_t workgroups;     /* workgroups of the main scan kernel */
     int32_t kernels;        /* kernels launched per call: the main scan, plus 2 when chunked
-                               (chunk aggregates, carry combine), plus 1 for bf16 io (the
-                               pre-pass that widens the B rows to fp32), plus 1 with
+                               (chunk aggregates, carry combine), plus 1 with
                                VIMSCAN_FLAG_AUX_SWAP */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */
     size_t workspace_bytes; /* scratch this call needs: chunk carries and delta sums when
-                               chunks > 1, chunk_len*64*4 bytes per wave pair when
-                               park_in_workspace, and the widened fp32 B rows
-                               (2*batch*seqlen*16*4 bytes, half that forward only) for bf16
-                               io */
+                               chunks > 1, and chunk_len*64*4 bytes per wave pair when
+                               park_in_workspace (0: no workspace needed) */
 } vimscan_plan;
 
 /*
