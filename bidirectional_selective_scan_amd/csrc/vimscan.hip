@@ -368,7 +368,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
                                      int kend, float& dsum) {
     constexpr bool kConv = kVar == kWithConv;
     constexpr bool kOrd = kVar == kOrdered;
-    constexpr int P = kConv ? 3 : 4;  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
+    constexpr int P = kConv ? 5 : 6;  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
     constexpr uint32_t e = IoTraits<IO>::bytes;
     constexpr bool kReadout = kMode != kAggregate;
     using E = typename IoTraits<IO>::elem;
