@@ -602,45 +602,49 @@ __device__ __forceinline__ const void* region_rows(const ScanArgs& a, int reg, i
 
 template <typename IO>
 __device__ __forceinline__ void stage_rows(const ScanArgs& a, const WgCoords& c, float* lds, bool uni, bool withC) {
-    constexpr int kU = 16;                                     // words per thread per pass
+    constexpr int kU = 4;                                      // words per region per thread and pass
     constexpr int kPerWord = 4 / IoTraits<IO>::bytes;          // values per 32-bit word
     using El = typename IoTraits<IO>::elem;
     const int len = c.t1 - c.t0;
     const int64_t off = (static_cast<int64_t>(c.seq) * a.Lp + c.t0) * kN;
-    const int wpd = len * kN / kPerWord;                       // words per (matrix, direction)
+    const int wpd = len * kN / kPerWord;                       // words per region
     const int ndir = uni ? 1 : 2;
     const int first = withC ? 0 : ndir;                        // first region: C forward, or B forward
-    const int nreg = 2 * ndir - first;                         // regions staged
-    const int nw = nreg * wpd;                                 // words to stage
-    const uint32_t* src[4];  // rows of regions first .. first + nreg - 1 in memory (uniform pointers)
+    const int nreg = 2 * ndir - first;                         // regions staged (wave-uniform, 1..4)
+    const uint32_t* src[4];                                    // their rows in memory
+    float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-        src[r] = reinterpret_cast<const uint32_t*>(static_cast<const El*>(region_rows(a, min(first + r, 2 * ndir - 1), ndir)) + off);
+    for (int r = 0; r < 4; ++r) {
+        const int reg = min(first + r, 2 * ndir - 1);
+        src[r] = reinterpret_cast<const uint32_t*>(static_cast<const El*>(region_rows(a, reg, ndir)) + off);
+        sc[r] = reg < ndir ? kLn2 : 1.0f;
+    }
     const int nt = static_cast<int>(blockDim.x);
-    for (int base = static_cast<int>(threadIdx.x); base < nw; base += kU * nt) {
-        uint32_t w[kU];
+    // a pass moves the same kU word indices of every region: all loads are issued before any store
+    for (int base = static_cast<int>(threadIdx.x); base < wpd; base += kU * nt) {
+        uint32_t w[4][kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int i = base + u * nt;
-            const int r = min(i / wpd, nreg - 1);
-            const uint32_t* q = r == 0 ? src[0] : r == 1 ? src[1] : r == 2 ? src[2] : src[3];
-            w[u] = i < nw ? q[i - r * wpd] : 0u;
-        }
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int i = base + u * nt;
-            if (i < nw) {
-                const int r = i / wpd;
-                const float sc = first + r < ndir ? kLn2 : 1.0f;
-                float* dst = lds + r * a.T * kN + (i - r * wpd) * kPerWord;
-                if (kPerWord == 1) {
-                    dst[0] = __uint_as_float(w[u]) * sc;
-                } else {
-                    dst[0] = __uint_as_float(w[u] << 16) * sc;
-                    dst[1] = __uint_as_float(w[u] & 0xffff0000u) * sc;
+            for (int u = 0; u < kU; ++u) {
+                const int i = base + u * nt;
+                w[r][u] = (r < nreg && i < wpd) ? src[r][i] : 0u;
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int i = base + u * nt;
+                if (r < nreg && i < wpd) {
+                    float* dst = lds + r * a.T * kN + i * kPerWord;
+                    if (kPerWord == 1) {
+                        dst[0] = __uint_as_float(w[r][u]) * sc[r];
+                    } else {
+                        dst[0] = __uint_as_float(w[r][u] << 16) * sc[r];
+                        dst[1] = __uint_as_float(w[r][u] & 0xffff0000u) * sc[r];
+                    }
                 }
             }
-        }
     }
 }
 
