@@ -650,9 +650,10 @@ __device__ __forceinline__ void stage_rows(const ScanArgs& a, const WgCoords& c,
 
 // The same for a scan in a given order (both directions, C and B): the chunk's rows are gathered
 // in step order (row k of a region is the row of the token the order lists for step t0 + k), so
-// the walk reads them exactly as in raster order. One thread per (region, row): one lookup in the
-// order, then the row's words as independent loads, so a pass costs two dependent memory round
-// trips whatever the row's width.
+// the walk reads them exactly as in raster order, and the chunk's order entries are copied after
+// the rows (the walk's token lookups then read LDS). One thread per step: one lookup in the
+// order, then the words of that token's row in every region as independent loads, so a chunk of
+// up to blockDim.x steps costs two dependent memory round trips.
 template <typename IO>
 __device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCoords& c, float* lds, bool withC) {
     constexpr int kPerWord = 4 / IoTraits<IO>::bytes;
@@ -662,27 +663,36 @@ __device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCo
     const int64_t srow = static_cast<int64_t>(c.seq) * a.Lp;
     const int32_t* ord = a.order + srow + c.t0;
     const int first = withC ? 0 : 2;
-    const int nrows = (4 - first) * len;
-    int32_t* lds_ord = reinterpret_cast<int32_t*>(lds + (4 - first) * a.T * kN);  // after the rows
-    for (int i = static_cast<int>(threadIdx.x); i < len; i += static_cast<int>(blockDim.x)) lds_ord[i] = ord[i];
-    for (int i = static_cast<int>(threadIdx.x); i < nrows; i += static_cast<int>(blockDim.x)) {
-        const int r = i / len, k = i - r * len;  // region (from first) and step
-        const int reg = first + r;
-        const int tok = min(max(static_cast<int>(ord[k]), 0), a.Lp - 1);
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const El*>(region_rows(a, reg, 2)) +
-                                                                (srow + tok) * kN);
-        uint32_t w[wpr];
+    const int nreg = 4 - first;  // regions staged (wave-uniform)
+    int32_t* lds_ord = reinterpret_cast<int32_t*>(lds + nreg * a.T * kN);  // after the rows
+    for (int k = static_cast<int>(threadIdx.x); k < len; k += static_cast<int>(blockDim.x)) {
+        const int32_t o = ord[k];
+        lds_ord[k] = o;
+        const int tok = min(max(static_cast<int>(o), 0), a.Lp - 1);
+        uint32_t w[4][wpr];
 #pragma unroll
-        for (int q = 0; q < wpr; ++q) w[q] = src[q];
-        const float sc = reg < 2 ? kLn2 : 1.0f;
-        float* dst = lds + r * a.T * kN + k * kN;
+        for (int r = 0; r < 4; ++r) {
+            if (r < nreg) {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                    static_cast<const El*>(region_rows(a, first + r, 2)) + (srow + tok) * kN);
 #pragma unroll
-        for (int q = 0; q < wpr; ++q) {
-            if (kPerWord == 1) {
-                dst[q] = __uint_as_float(w[q]) * sc;
-            } else {
-                dst[2 * q] = __uint_as_float(w[q] << 16) * sc;
-                dst[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u) * sc;
+                for (int q = 0; q < wpr; ++q) w[r][q] = src[q];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (r < nreg) {
+                const float sc = first + r < 2 ? kLn2 : 1.0f;
+                float* dst = lds + r * a.T * kN + k * kN;
+#pragma unroll
+                for (int q = 0; q < wpr; ++q) {
+                    if (kPerWord == 1) {
+                        dst[q] = __uint_as_float(w[r][q]) * sc;
+                    } else {
+                        dst[2 * q] = __uint_as_float(w[r][q] << 16) * sc;
+                        dst[2 * q + 1] = __uint_as_float(w[r][q] & 0xffff0000u) * sc;
+                    }
+                }
             }
         }
     }
