@@ -62,6 +62,7 @@ SHAPES = [
     (2, 102, 33, 51, 0),
     (1, 60, 64, 1, 0),       # reset every token
     (3, 256, 64, 0, 0),      # the longest single-pass sequence
+    (1, 512, 64, 0, 256),    # 256-token chunks: the largest LDS row staging (64 KB), park in the workspace
 ]
 
 

@@ -52,6 +52,8 @@ CASES = [
     (1, 6 * 51, 96, "bf16", 51, 0, "random"),    # folded: an order per segment
     (3, 4 * 20, 64, "f32", 20, 16, "deformable"),
     (1, 1, 64, "f32", 0, 0, "random"),
+    (1, 256, 64, "bf16", 0, 256, "random"),     # one 256-token chunk: rows and order in LDS (66.5 KB)
+    (1, 512, 64, "f32", 0, 256, "hilbert"),     # two of them, with a carry
 ]
 
 
