@@ -44,7 +44,7 @@
 //    sequence's B/C rows) land on the same XCD and its L2.
 //  * Variants of the same kernels (a template parameter): the directional convolution in front
 //    of each direction (a register window of the previous raw inputs in walk order), and the scan
-//    in a given token order (a step's token is looked up in the order through the scalar unit;
+//    in a given token order (a step's token is looked up in the chunk's copy of the order in LDS;
 //    chunks are ranges of steps, B and C rows are gathered into LDS in step order, so the park,
 //    the meeting point and the chunk carries stay indexed by step).
 
@@ -354,10 +354,10 @@ __device__ __forceinline__ uint32_t ld_global_raw(const void* base, int64_t i) {
 // Walk this wave's tokens k = kbeg..kend-1 of the chunk (forward: local token k; backward:
 // local token len-1-k). Per step k: the prelude of token k+1 (including delta*x*B) is formed
 // from a ring of prefetched x/dt values (refilled P tokens ahead) and the B row of token k+1,
-// after which the B row of token k+2 is requested through the scalar unit; z and the parked
-// value of token k come from their own ring; token k's state update and readout run on the
-// prelude formed a step earlier, with the C row read from LDS a step earlier. Every prefetch
-// index is clamped into the walk, so every load stays inside the chunk.
+// read from the chunk's rows in LDS; z and the parked value of token k come from their own ring;
+// token k's state update and readout run on the prelude formed a step earlier, with the C row of
+// token k read from LDS in the same step. Every prefetch index is clamped into the walk, so every
+// load stays inside the chunk.
 // With kConv each direction's input is u = silu(cbias + taps . x) over the current token and
 // the three before it in walk order (a register window; at the walk's first step the window is
 // loaded from the tokens before it, which may lie in the neighbouring chunk, and is zero
