@@ -383,8 +383,13 @@ __device__ __forceinline__ void out_tiles(const NcArgs& a, int64_t row0, int d0,
 // read out at once; it never goes to memory. One workgroup per (channel block, sequence), channel
 // block fastest.
 
+// bf16 with N = 16 (the Vim shapes) is asked for 6 waves per SIMD: left alone the compiler used
+// 84 VGPRs, which allocate as 88 and fit 5, so a grid of 6 waves per SIMD ran as one full and one
+// partial generation; at 70 VGPRs (no spills) it is a single generation.
 template <typename IO, int NB>
-__global__ __launch_bounds__(256) void k_ncssd_fused(NcArgs a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(sizeof(typename Io<IO>::elem) == 2 && NB == 1 ? 6 : 1)))
+void k_ncssd_fused(NcArgs a) {
     __shared__ float4 red[kWaves][4 * NB][64];
     __shared__ __attribute__((aligned(16))) uint32_t stage[kWaves][kStageWords<IO>];
     const int lane = static_cast<int>(threadIdx.x) & 63;
