@@ -491,6 +491,9 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         xr[0] = ld_raw(IO{}, rx, vo, so);
         dr[0] = ld_raw(IO{}, rd, vo, so);
     }
+    // In a given order the token of each refill is read from LDS a step before the refill that
+    // uses it, so the lookup's latency is not on the path of the step's loads.
+    int tla = kOrd ? trow(kbeg + 1 + P) : 0;
 
     auto body = [&](int kk, int j) {  // step kk, ring slot j = (kk - kbeg) % P
         const int jn = (j + 1) % P;
@@ -510,8 +513,9 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         {
             uint32_t so;
             if constexpr (kOrd) {
-                tx[jn] = trow(kk + 1 + P);
+                tx[jn] = tla;  // step kk + 1 + P, looked up during the previous step
                 so = tokoff(tx[jn]);
+                tla = trow(kk + 2 + P);
             } else {
                 so = toff(kk + 1 + P);
             }
