@@ -79,6 +79,58 @@ def make_inputs(batch: int, seqlen: int, d_inner: int, d_state: int = 16, io_dty
     return out
 
 
+def _device_normal(shape, std, dtype, g, device, slab=1 << 26):
+    """A tensor of N(0, std^2) draws made on the device in slabs along dim 1 (bounded temporaries),
+    rounded to ``dtype``."""
+    import torch
+    out = torch.empty(shape, dtype=dtype, device=device)
+    per = max(1, slab // max(1, shape[0] * int(np.prod(shape[2:]))))
+    for t0 in range(0, shape[1], per):
+        t1 = min(shape[1], t0 + per)
+        part = torch.randn((shape[0], t1 - t0) + tuple(shape[2:]), generator=g, device=device)
+        out[:, t0:t1] = (part * std).to(dtype)
+    return out
+
+
+def device_inputs(batch: int, seqlen: int, d_inner: int, d_state: int = 16, io_dtype: str = "bf16",
+                  seed: int = 0, device: str = "cuda:0") -> dict:
+    """The scan's input recipe drawn on a device, for sizes too large to draw on the host: x, z ~
+    N(0, 1), dt ~ N(0, 0.5^2) (batch, seqlen, d_inner) and B_f, C_f, B_b, C_b ~ N(0, 1) (batch,
+    seqlen, d_state) from one seeded torch generator on the device (a different stream of numbers
+    than make_inputs at the same seed), rounded to the io dtype; the parameters are make_inputs'
+    (they do not depend on the length). Returns torch tensors on the device."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = torch.bfloat16 if io_dtype == "bf16" else torch.float32
+    out = {}
+    for name, std in (("x", 1.0), ("z", 1.0), ("dt", 0.5)):
+        out[name] = _device_normal((batch, seqlen, d_inner), std, tdt, g, device)
+    for name in ("B_f", "C_f", "B_b", "C_b"):
+        out[name] = _device_normal((batch, seqlen, d_state), 1.0, tdt, g, device)
+    params = make_inputs(1, 1, d_inner, d_state, "f32", seed)
+    for name in PARAM_NAMES:
+        out[name] = torch.from_numpy(params[name]).to(device)
+    return out
+
+
+def device_ncssd_inputs(batch: int, seqlen: int, d_inner: int, d_state: int = 16, io_dtype: str = "bf16",
+                        seed: int = 0, device: str = "cuda:0") -> dict:
+    """ncssd_inputs' recipe drawn on a device (x, B, C ~ N(0, 1) rounded to the io dtype;
+    m = exp(exp(u)), u ~ U(ln 1e-3, 0), float32), for sizes too large to draw on the host."""
+    import math
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = torch.bfloat16 if io_dtype == "bf16" else torch.float32
+    out = {"x": _device_normal((batch, seqlen, d_inner), 1.0, tdt, g, device)}
+    for name in ("B", "C"):
+        out[name] = _device_normal((batch, seqlen, d_state), 1.0, tdt, g, device)
+    u = torch.rand((batch, seqlen), generator=g, device=device) * (-math.log(1e-3)) + math.log(1e-3)
+    out["m"] = torch.exp(torch.exp(u)).to(torch.float32)
+    return out
+
+
 def make_workload_inputs(w: Workload) -> dict:
     return make_inputs(w.batch, w.seqlen, w.d_inner, w.d_state, w.io_dtype, w.seed)
 

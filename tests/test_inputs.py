@@ -81,3 +81,21 @@ def test_ncssd_inputs_recipe():
     for k in ("x", "B", "C"):
         np.testing.assert_array_equal(round_to_io(a[k], "bf16"), a[k])
     assert (a["m"] > 1.0).all() and (a["m"] <= np.float32(np.e)).all()
+
+
+def test_device_generators_follow_the_recipe():
+    """device_inputs / device_ncssd_inputs (used where the host cannot draw the inputs): seeded,
+    the stated distributions, the io dtype, and make_inputs' parameters."""
+    from bidirectional_selective_scan_amd.inputs import device_inputs, device_ncssd_inputs
+    a = device_inputs(2, 3000, 64, 16, "bf16", seed=3, device="cpu")
+    b = device_inputs(2, 3000, 64, 16, "bf16", seed=3, device="cpu")
+    for k in a:
+        assert torch.equal(a[k], b[k])
+    assert a["x"].dtype == torch.bfloat16 and a["B_f"].shape == (2, 3000, 16)
+    assert abs(a["x"].float().std().item() - 1) < 0.02 and abs(a["dt"].float().std().item() - 0.5) < 0.01
+    ref = make_inputs(1, 1, 64, 16, "f32", 3)
+    for k in ("A_f", "A_b", "D_f", "D_b", "dt_bias_f", "dt_bias_b"):
+        np.testing.assert_array_equal(a[k].numpy(), ref[k])
+    n = device_ncssd_inputs(1, 5000, 32, 16, "f32", seed=4, device="cpu")
+    m = n["m"].numpy()
+    assert n["x"].dtype == torch.float32 and m.min() > 1.0 and m.max() <= np.e * (1 + 1e-6)
