@@ -50,6 +50,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -877,6 +878,40 @@ constexpr int64_t kLdsParkMaxBytes = 20 * 1024;
 constexpr int64_t kUniSinglePass = 1024;
 constexpr int64_t kUniTarget = 3072;
 
+// An MI355X: 256 compute units with 160 KB of LDS each.
+constexpr int64_t kCus = 256;
+constexpr int64_t kLdsPerCu = 160 * 1024;
+
+// Workgroups of a chunked scan pass that one CU holds at once. The register budget of the scan
+// kernels (about 150-160 VGPRs with bf16 io, 175-200 with fp32) allows 3 waves per SIMD with bf16
+// and 2 with fp32, one wave of each workgroup on each SIMD; the bidirectional kernel's LDS (rows,
+// the order and a park in LDS) can allow fewer.
+int64_t resident_wgs(const Plan* p, int io_dtype, int64_t T) {
+    int64_t r = io_dtype == VIMSCAN_BF16 ? 3 : 2;
+    if (!p->uni) {
+        const bool lds_park = T * kWave * static_cast<int64_t>(sizeof(float)) <= kLdsParkMaxBytes;
+        const int64_t bytes = (4 * T * kN + T + (lds_park ? p->subs * T * kWave : 0)) * sizeof(float);
+        if (kLdsPerCu / bytes < r) r = kLdsPerCu / bytes;
+    }
+    return r;
+}
+
+// Modelled time of a chunked pass with chunks of T tokens. The busiest CU runs ceil(wgs / 256)
+// workgroups, in rounds of at most resident_wgs; a round of a workgroups on a CU costs a / e(a)
+// per token, e(a) being the issue efficiency of the VALU-bound token loop with a waves per SIMD
+// (about 0.5 for a lone wave, 0.9 and more from two on, as measured on this kernel), and each
+// chunk adds about 8 tokens' worth of fixed work (staging, carries).
+double chunk_cost(const Plan* p, int io_dtype, int64_t T) {
+    static const double eff[4] = {0.5, 0.9, 0.92, 0.95};
+    const int64_t K = (p->Lp + T - 1) / T;
+    const int64_t wgs = p->nseq * K * ((p->ncb + p->subs - 1) / p->subs);
+    const int64_t per_cu = (wgs + kCus - 1) / kCus;
+    const int64_t r = resident_wgs(p, io_dtype, T);
+    auto round_cost = [&](int64_t a) { return a / eff[a < 4 ? a - 1 : 3]; };
+    const int64_t rounds = per_cu / r, rest = per_cu % r;
+    return static_cast<double>(T + 8) * (rounds * round_cost(r) + (rest ? round_cost(rest) : 0.0));
+}
+
 const char* const kStatusText[] = {
     "ok",
     "a required pointer is NULL",
@@ -930,30 +965,43 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     // forward only; a chunked plan aims at 1536 of them (3 waves per SIMD bidirectional).
     const int64_t lanes = p->nseq * p->ncb;
     const int64_t target = p->uni ? kUniTarget : 1536;
-    int64_t T;
-    if (l->chunk_len > 0) {
-        T = l->chunk_len;
-    } else if ((p->Lp <= kMaxChunk && lanes >= (p->uni ? kUniSinglePass : 256)) || p->Lp <= 32) {
-        T = p->Lp;  // single pass: enough workgroups, or too short to be worth chunking
-    } else {
-        // Chunk for parallelism with at least 32 tokens per chunk.
-        int64_t K = (target + lanes - 1) / lanes;
-        const int64_t kmin = (p->Lp + kMaxChunk - 1) / kMaxChunk;
-        const int64_t kmax = (p->Lp + 31) / 32;
-        if (K < kmin) K = kmin;
-        if (K > kmax) K = kmax;
-        T = (p->Lp + K - 1) / K;
-    }
-    if (T > p->Lp) T = p->Lp;
-    if (T > kMaxChunk) T = kMaxChunk;
-    p->T = T;
-    p->K = (p->Lp + T - 1) / T;
     // Four waves per workgroup (two channel blocks x two directions, or four channel blocks
     // forward only) when there are enough channel blocks: the hardware spreads a 4-wave
     // workgroup over the CU's four SIMDs, where 2-wave workgroups can leave some SIMDs with twice
     // the waves of others.
     if (p->uni) p->subs = p->ncb >= 4 ? 4 : p->ncb;
     else p->subs = p->ncb >= 2 ? 2 : 1;
+    int64_t T;
+    if (l->chunk_len > 0) {
+        T = l->chunk_len;
+    } else if ((p->Lp <= kMaxChunk && lanes >= (p->uni ? kUniSinglePass : 256)) || p->Lp <= 32) {
+        T = p->Lp;  // single pass: enough workgroups, or too short to be worth chunking
+    } else {
+        // Chunk for parallelism: first enough chunks for `target` waves, with at least 32 tokens
+        // per chunk.
+        int64_t K = (target + lanes - 1) / lanes;
+        const int64_t kmin = (p->Lp + kMaxChunk - 1) / kMaxChunk;
+        const int64_t kmax = (p->Lp + 31) / 32;
+        if (K < kmin) K = kmin;
+        if (K > kmax) K = kmax;
+        // When that leaves only a few rounds of workgroups per CU, a round that is partly empty
+        // costs as much as a full one: take instead the chunk count of least modelled time, up
+        // to twice as many chunks and down to 16 tokens per chunk.
+        const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;
+        if (p->nseq * K * wpc <= 4 * kCus * resident_wgs(p, l->io_dtype, (p->Lp + K - 1) / K)) {
+            const int64_t khi = std::min((p->Lp + 15) / 16, 2 * K);
+            double best = -1.0;
+            for (int64_t k = kmin; k <= khi; ++k) {
+                const double c = chunk_cost(p, l->io_dtype, (p->Lp + k - 1) / k);
+                if (best < 0.0 || c < best) best = c, K = k;
+            }
+        }
+        T = (p->Lp + K - 1) / K;
+    }
+    if (T > p->Lp) T = p->Lp;
+    if (T > kMaxChunk) T = kMaxChunk;
+    p->T = T;
+    p->K = (p->Lp + T - 1) / T;
     p->wgs = p->nseq * p->K * ((p->ncb + p->subs - 1) / p->subs);
     p->kernels = (p->K > 1 ? 3 : 1) + (p->swap ? 1 : 0);
     p->park_global = !p->uni && p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
