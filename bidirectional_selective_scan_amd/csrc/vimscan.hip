@@ -162,11 +162,17 @@ struct ScanArgs {
     int conv_k;          // taps, 1..kMaxTaps; 0 without the convolution
     int uni;             // 1: forward only (vimscan_fwd): every wave of a workgroup is a channel block
     const int32_t* order;  // kOrdered: [nseq][Lp] the token each scan step visits (vimscan_bidir_order_fwd)
+    int fold;              // chunked: 1 when each scan workgroup folds the chunk aggregates itself
 };
 
 // Taps of the directional convolution the kernels carry (a layer with fewer taps is run with
 // the missing ones at zero).
 constexpr int kMaxTaps = 4;
+
+// Plans of up to kFoldMaxChunks chunks run without the carry combine kernel: each scan workgroup
+// folds the aggregates before its chunk itself, kFoldBatch chunks per round of loads.
+constexpr int kFoldMaxChunks = 32;
+constexpr int kFoldBatch = 4;
 
 // What a scan kernel instance does besides the plain bidirectional scan.
 enum Variant {
@@ -706,6 +712,37 @@ __device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCo
 // Main scan: one chunk of one sequence, 64 channels; wave 0 forward, wave 1 backward. The waves
 // meet in the middle of the chunk through the park (LDS, or a global scratch region per
 // workgroup when the chunk is long; see the file header).
+// The state entering chunk `chunk` of direction dir, for the lane's channel dc: the chunk
+// aggregates of the chunks before it in scan order folded in the carry combine's order and
+// arithmetic (so bit for bit the combine's result). The loads go kFoldBatch chunks at a time, all
+// issued together, clamped to a chunk whose aggregate exists; only the first cnt enter the fold.
+__device__ __forceinline__ void fold_carry(const ScanArgs& a, int dir, int seq, int chunk, int dc, float (&h)[kN]) {
+    const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
+    const int cnt = dir == 0 ? chunk : a.K - 1 - chunk;  // chunks before this one in scan order
+    float an[kN];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) an[n] = a.A[dir][dc * kN + n];
+#pragma unroll
+    for (int n = 0; n < kN; ++n) h[n] = 0.0f;
+    for (int j0 = 0; j0 < cnt; j0 += kFoldBatch) {
+        float e[kFoldBatch][kN], sv[kFoldBatch];
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j) {
+            const int k = dir == 0 ? min(j0 + j, a.K - 2) : max(a.K - 1 - j0 - j, 1);
+            const int64_t slot = base + k;
+            sv[j] = a.dsum[slot * a.Di + dc];
+#pragma unroll
+            for (int n = 0; n < kN; ++n) e[j][n] = a.carry[(slot * kN + n) * a.Di + dc];
+        }
+#pragma unroll
+        for (int j = 0; j < kFoldBatch; ++j)
+            if (j0 + j < cnt) {
+#pragma unroll
+                for (int n = 0; n < kN; ++n) h[n] = fmaf(fast_exp2(an[n] * sv[j]), h[n], e[j][n]);
+            }
+    }
+}
+
 template <typename IO, bool kCarry, bool kGlobalPark, int kVar>
 __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     constexpr bool kConv = kVar == kWithConv;
@@ -722,7 +759,9 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     Lane ln;
     ln.init(a, c.dir, c.dc, kConv);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
-    if (kCarry) {
+    if (kCarry && a.fold) {
+        fold_carry(a, c.dir, c.seq, c.chunk, c.dc, ln.h);
+    } else if (kCarry) {
         const float* src = a.carry + ((static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = src[n * static_cast<int64_t>(a.Di) + c.dc];
@@ -750,7 +789,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
     stage_rows<IO>(a, c, lds, true, true);
     Lane ln;
     ln.init(a, 0, c.dc, true);
-    if (kCarry) {
+    if (kCarry && a.fold) {
+        fold_carry(a, 0, c.seq, c.chunk, c.dc, ln.h);
+    } else if (kCarry) {
         const float* src = a.carry + (static_cast<int64_t>(c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = src[n * static_cast<int64_t>(a.Di) + c.dc];
@@ -864,7 +905,7 @@ __global__ __launch_bounds__(256) void k_aux_swap(ScanArgs a) {
 struct Plan {
     int64_t nseq, Lp, T, K, ncb, subs, wgs;
     int kernels;
-    bool park_global, uni, swap;
+    bool park_global, uni, swap, fold;
     size_t ws;                                 // total scratch bytes
     size_t off_dsum, off_park;                // byte offsets of the regions after the carries
 };
@@ -1003,7 +1044,10 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     p->T = T;
     p->K = (p->Lp + T - 1) / T;
     p->wgs = p->nseq * p->K * ((p->ncb + p->subs - 1) / p->subs);
-    p->kernels = (p->K > 1 ? 3 : 1) + (p->swap ? 1 : 0);
+    // With few chunks every scan workgroup folds the aggregates before its chunk itself: no
+    // combine kernel, and the carries are written once and read, not rewritten.
+    p->fold = p->K > 1 && p->K <= kFoldMaxChunks;
+    p->kernels = (p->K > 1 ? (p->fold ? 2 : 3) : 1) + (p->swap ? 1 : 0);
     p->park_global = !p->uni && p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
     const size_t f = sizeof(float);
     const size_t ndir = p->uni ? 1 : 2;
@@ -1042,7 +1086,7 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
         hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
                            lds, s, a);
         const dim3 cgrid(static_cast<unsigned>(p.ncb * (p.uni ? 1 : 2) * p.nseq), 4);
-        hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
+        if (!p.fold) hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
     const bool timed = ev0 != nullptr && ev1 != nullptr;
     if (timed && hipEventRecord(ev0, s) != hipSuccess) return VIMSCAN_ERR_HIP;
@@ -1154,6 +1198,7 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.K = static_cast<int>(p.K);
     a.ncb = static_cast<int>(p.ncb);
     a.subs = static_cast<int>(p.subs);
+    a.fold = p.fold ? 1 : 0;
     a.general = (launch->flags & VIMSCAN_FLAG_GENERAL_DECAY) ? 1 : 0;
     a.cw[0] = conv ? conv->w_f : nullptr;
     a.cw[1] = conv ? conv->w_b : nullptr;

@@ -137,9 +137,10 @@ typedef struct vimscan_plan {
     int64_t chunk_len;      /* tokens per chunk */
     int64_t chunks;         /* chunks per sequence; 1 = single pass (no chunk carries) */
     int64_t workgroups;     /* workgroups of the main scan kernel */
-    int32_t kernels;        /* kernels launched per call: the main scan, plus 2 when chunked
-                               (chunk aggregates, carry combine), plus 1 with
-                               VIMSCAN_FLAG_AUX_SWAP */
+    int32_t kernels;        /* kernels launched per call: the main scan, plus 1 when chunked
+                               (chunk aggregates), plus 1 more beyond 32 chunks per sequence
+                               (carry combine; up to 32 the scan workgroups fold the aggregates
+                               themselves), plus 1 with VIMSCAN_FLAG_AUX_SWAP */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */
     size_t workspace_bytes; /* scratch this call needs: chunk carries and delta sums when

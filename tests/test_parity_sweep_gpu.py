@@ -98,3 +98,26 @@ def test_sweep_covers_every_variant_and_path():
     assert seen["general"] == {False, True}
     assert any(c["seg"] for c in CASES) and any(c["chunk"] for c in CASES)
     assert any(c["chunk"] == 0 and (c["seg"] or c["L"]) > 256 for c in CASES)   # the plan chunks by itself
+
+
+# Plans of up to this many chunks per sequence fold the chunk aggregates in the scan workgroups.
+FOLD_MAX_CHUNKS = 32
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("K", [2, 3, 4, 5, 6, 9, 16, FOLD_MAX_CHUNKS, FOLD_MAX_CHUNKS + 1])
+def test_chunk_counts_around_the_in_scan_fold(K, variant, io):
+    """A sequence of up to FOLD_MAX_CHUNKS chunks runs without the carry-combine kernel: each scan
+    workgroup folds the aggregates of the chunks before its own, four chunks per round of loads (one
+    round up to 5 chunks, several from 6); past that the combine supplies the entering states.
+    Every variant against the oracle at each count, with a ragged last chunk and a ragged channel
+    block, general transitions with fp32 io and geometric ones with bf16."""
+    T, Di = 7, 96
+    c = dict(variant=variant, io=io, params="random" if io == "f32" else "s4d", B=2, L=T * (K - 1) + 4, seg=0,
+             Di=Di, chunk=T, general=False, taps=3, seed=7000 + 10 * K + VARIANTS.index(variant))
+    info = binding.launch_info(c["B"], c["L"], Di, 16, 0, io, chunk_len=T,
+                               forward_only=variant in ("fwd", "fwd_swap"), aux_swap=variant == "fwd_swap")
+    assert info["chunks"] == K
+    assert info["kernels"] == (2 if K <= FOLD_MAX_CHUNKS else 3) + (1 if variant == "fwd_swap" else 0)
+    test_random_case_matches_oracle(c)
