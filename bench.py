@@ -139,6 +139,39 @@ def ncssd_leg(w, timed, stats_us, plan, nbytes, ncopies) -> dict:
                               "(high and low parts of B*m and H)"}}
 
 
+def configs_leg(graph_wall, dev, steps):
+    """Every workload at its full size (tiny, Vim-Ti, Vim-S, high-res, folded), timed as HIP graph
+    replays of the whole library call with the plan's own chunking, on inputs drawn on the device
+    with the same distributions; rotating input copies past the Infinity Cache (at most 64)."""
+    import torch
+    from bidirectional_selective_scan_amd import binding
+    from bidirectional_selective_scan_amd.configs import WORKLOADS
+    from bidirectional_selective_scan_amd.inputs import device_inputs
+    io_names = ("x", "dt", "z", "B_f", "C_f", "B_b", "C_b")
+    par_names = ("A_f", "A_b", "D_f", "D_b", "dt_bias_f", "dt_bias_b")
+    res = {}
+    for w in WORKLOADS:
+        inp = device_inputs(w.batch, w.seqlen, w.d_inner, 16, w.io_dtype, seed=0, device=str(dev))
+        nbytes = w.algorithmic_bytes()
+        n = min(64, max(2, -(-2 * CACHE_BYTES // nbytes) + 1))
+        copies = [[inp[k].clone() for k in io_names] for _ in range(n)]
+        outs = [torch.empty_like(inp["x"]) for _ in range(n)]
+        params = [inp[k] for k in par_names]
+        plan = binding.launch_info(w.batch, w.seqlen, w.d_inner, 16, w.seg_len, w.io_dtype)
+        ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+        wall = graph_wall(lambda i, s: binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i],
+                                                            workspace=ws, stream=s), ncopy=n, warmup=200)
+        step = wall / steps
+        ops = alu_ops_per_element(True) * w.tokens_channels
+        res[w.name] = {"us_per_call": round(step * 1e6, 3), "gbs": round(nbytes / step / 1e9, 2),
+                       "pct_hbm_peak": round(100 * nbytes / step / 1e9 / HBM_PEAK_GBS, 2),
+                       "tokens_channels_per_s": round(w.tokens_channels / step, 1),
+                       "alu_frac": round(ops / step / 1e12 / VALU_PEAK_TOPS, 4),
+                       "plan": {k: plan[k] for k in ("chunk_len", "chunks", "workgroups", "kernels")}}
+        del copies, outs, inp, ws
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +191,8 @@ def main(argv=None):
                     help="skip the scan in a given token order (7 x 7 local windows of the patch grid)")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the scan on one GPU's share of an 8-way batch split (batch / 8)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config timings (every workload, graph replays of the whole call)")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy bandwidth ceiling")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the headline steps as eager library calls instead of HIP graph replays")
@@ -285,10 +320,11 @@ def main(argv=None):
     wall, per_call, per_scan = timed(False)
     kernel_s = float(np.mean(per_scan))
     launch_mode = "eager library calls"
-    def graph_wall(make):
+    def graph_wall(make, ncopy=ncopy, warmup=None):
         """Wall time of args.steps steps replayed from HIP graphs, each step the whole library call
         (every kernel of the path) on input copy i % ncopy; make(i, stream) prepares that call on
         the given stream. One graph holds ncopy consecutive steps, single-step graphs the rest."""
+        warmup = args.warmup if warmup is None else warmup
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -304,7 +340,7 @@ def main(argv=None):
             return g
         block = capture(range(ncopy))
         singles = [capture([i]) for i in range(ncopy)]
-        for i in range(args.warmup):
+        for i in range(warmup):
             singles[i % ncopy].replay()
         torch.cuda.synchronize(dev)
         t0 = time.perf_counter()
@@ -454,6 +490,8 @@ def main(argv=None):
                                "scan_kernel_us": round(ks * 1e6, 3),
                                "alu_frac_step": round(ops / 8 / step_s / 1e12 / VALU_PEAK_TOPS, 4),
                                "plan": {k: plan_s[k] for k in ("chunks", "workgroups", "park_in_workspace")}}
+    if not args.no_configs and not args.no_graph:
+        out["configs"] = configs_leg(graph_wall, dev, args.steps)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out), flush=True)

@@ -1012,10 +1012,16 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
     // the waves of others.
     if (p->uni) p->subs = p->ncb >= 4 ? 4 : p->ncb;
     else p->subs = p->ncb >= 2 ? 2 : 1;
+    const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;  // workgroups per sequence and chunk
+    // A bidirectional single pass with at most one workgroup per CU gives each SIMD a lone wave
+    // (Vim-Ti: 192 workgroups on 256 CUs): from 64 tokens on, chunking to the wave-pair target
+    // pays for the aggregate pass (Vim-Ti: 4 chunks of 50, 72.9 -> 66.0 us per call).
+    const bool single = (p->Lp <= kMaxChunk && lanes >= (p->uni ? kUniSinglePass : 256)) || p->Lp <= 32;
+    const bool sparse = single && !p->uni && p->Lp >= 64 && p->nseq * wpc <= kCus;
     int64_t T;
     if (l->chunk_len > 0) {
         T = l->chunk_len;
-    } else if ((p->Lp <= kMaxChunk && lanes >= (p->uni ? kUniSinglePass : 256)) || p->Lp <= 32) {
+    } else if (single && !sparse) {
         T = p->Lp;  // single pass: enough workgroups, or too short to be worth chunking
     } else {
         // Chunk for parallelism: first enough chunks for `target` waves, with at least 32 tokens
@@ -1028,8 +1034,7 @@ int make_plan(const vimscan_launch* l, int64_t seg_len, Plan* p) {
         // When that leaves only a few rounds of workgroups per CU, a round that is partly empty
         // costs as much as a full one: take instead the chunk count of least modelled time, up
         // to twice as many chunks and down to 16 tokens per chunk.
-        const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;
-        if (p->nseq * K * wpc <= 4 * kCus * resident_wgs(p, l->io_dtype, (p->Lp + K - 1) / K)) {
+        if (!sparse && p->nseq * K * wpc <= 4 * kCus * resident_wgs(p, l->io_dtype, (p->Lp + K - 1) / K)) {
             const int64_t khi = std::min((p->Lp + 15) / 16, 2 * K);
             double best = -1.0;
             for (int64_t k = kmin; k <= khi; ++k) {

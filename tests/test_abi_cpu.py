@@ -68,8 +68,14 @@ def test_plans_for_the_workloads(lib):
     carry = 2 * 8 * hi["chunks"] * 16 * 768 * 4
     dsum = 2 * 8 * hi["chunks"] * 768 * 4
     assert hi["workspace_bytes"] == carry + dsum
+    # Vim-Ti in one pass would be 192 workgroups, one per CU at most: it is cut into 4 chunks of 50
+    # (768 workgroups), with the carries and delta sums in the workspace and the park in LDS
     ti = binding.launch_info(64, 197, 384, 16, 0, "f32")
-    assert ti["kernels"] == 1 and ti["workspace_bytes"] == ti["workgroups"] * 2 * 197 * 64 * 4
+    assert (ti["chunk_len"], ti["chunks"], ti["workgroups"], ti["kernels"]) == (50, 4, 768, 2)
+    carry, dsum = 2 * 64 * 4 * 16 * 384 * 4, 2 * 64 * 4 * 384 * 4
+    assert ti["park_in_workspace"] == 0 and ti["workspace_bytes"] == carry + dsum
+    one_pass = binding.launch_info(64, 197, 384, 16, 0, "f32", chunk_len=197)
+    assert one_pass["kernels"] == 1 and one_pass["workspace_bytes"] == one_pass["workgroups"] * 2 * 197 * 64 * 4
     # a forced chunk length is honoured and capped at 256 tokens
     assert binding.launch_info(2, 197, 64, chunk_len=16)["chunks"] == 13
     assert binding.launch_info(1, 1000, 64, chunk_len=5000)["chunk_len"] == 256
