@@ -117,7 +117,7 @@ def cpu_baseline(inp: dict, w) -> dict:
                       f"({round(3 * t * cores, 1)} core-seconds in all)"}
 
 
-def ncssd_leg(w, timed, stats_us, plan, nbytes, ncopies) -> dict:
+def ncssd_leg(w, timed, stats_us, plan, nbytes, ncopies, value_wall=None, launch="eager library calls") -> dict:
     """The NC-SSD global-state form y = C (B^T (x . m)) on the workload's shape: HBM roofline of
     the call (its kernels bracketed by the library's events) and the matrix-core rate."""
     wall, per_call, per_kern = timed("ncssd")
@@ -127,8 +127,8 @@ def ncssd_leg(w, timed, stats_us, plan, nbytes, ncopies) -> dict:
     gbs = nbytes / k / 1e9
     kernel = "k_ncssd_fused" if plan["chunks"] == 1 else "k_ncssd_state + k_ncssd_reduce + k_ncssd_out"
     return {"what": "NC-SSD global-state form y = C (B^T (x . m)), N = 16 (vimscan_ncssd_fwd)",
-            "value": round(nbytes * len(per_call) / wall / 1e9, 2), "unit": "GB/s",
-            "call_us": stats_us(per_call), "kernel_us": round(k * 1e6, 3), "kernels_per_step": plan["kernels"],
+            "value": round(nbytes * len(per_call) / (value_wall(wall) if value_wall else wall) / 1e9, 2),
+            "unit": "GB/s", "launch": launch, "call_us": stats_us(per_call), "kernel_us": round(k * 1e6, 3), "kernels_per_step": plan["kernels"],
             "input_copies": ncopies, "algorithmic_bytes": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": kernel,
@@ -237,18 +237,25 @@ def main(argv=None):
     if plan["workspace_bytes"]:
         ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
 
-    calls = {g: [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
-                                      general_decay=g) for i in range(ncopy)] for g in (False, True)}
+    # mk[leg](i, stream) prepares the leg's call on input copy i (queued on `stream`, or torch's
+    # current stream): eager calls time each call, graph replays of the same calls give `value`
+    mk = {}
+    for g in (False, True):
+        mk[g] = (lambda g: lambda i, st=None: binding.PreparedCall(
+            *copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws, general_decay=g, stream=st))(g)
+    calls = {g: [mk[g](i) for i in range(ncopy)] for g in (False, True)}
     from bidirectional_selective_scan_amd.inputs import conv_params
     cp = conv_params(w.d_inner, 4, w.seed + 101)
     conv = tuple(torch.from_numpy(cp[k]).to(dev) for k in ("conv_w_f", "conv_b_f", "conv_w_b", "conv_b_b"))
-    calls["conv"] = [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
-                                          conv=conv) for i in range(ncopy)]
+    mk["conv"] = lambda i, st=None: binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i],
+                                                         workspace=ws, conv=conv, stream=st)
+    calls["conv"] = [mk["conv"](i) for i in range(ncopy)]
     # forward only: x, dt, z, B_f, C_f and the forward parameters of the same inputs
     for name, swap in (("fwd", False), ("fwd_swap", True)):
-        calls[name] = [binding.prepare_fwd(copies[i][0], copies[i][1], copies[i][2], copies[i][3], copies[i][4],
-                                           params[0], params[2], params[4], seg_len=w.seg_len, out=outs[i],
-                                           aux_swap=swap) for i in range(ncopy)]
+        mk[name] = (lambda swap: lambda i, st=None: binding.prepare_fwd(
+            copies[i][0], copies[i][1], copies[i][2], copies[i][3], copies[i][4], params[0], params[2], params[4],
+            seg_len=w.seg_len, out=outs[i], aux_swap=swap, stream=st))(swap)
+        calls[name] = [mk[name](i) for i in range(ncopy)]
 
     # the same scan in a given token order: local windows of the patch grid (the grid is the
     # largest square the sequence holds; the remaining tokens keep their place)
@@ -257,8 +264,9 @@ def main(argv=None):
     side = int(np.sqrt(T - 1)) if T > 1 else 1
     order_np = np.tile(grid_order("local", side, T, window=max(1, (side + 1) // 2)), (w.batch * w.seqlen // T, 1))
     order = torch.from_numpy(np.ascontiguousarray(order_np, dtype=np.int32)).to(dev)
-    calls["order"] = [binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i], workspace=ws,
-                                           order=order) for i in range(ncopy)]
+    mk["order"] = lambda i, st=None: binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i],
+                                                          workspace=ws, order=order, stream=st)
+    calls["order"] = [mk["order"](i) for i in range(ncopy)]
     order_desc = f"{side} x {side} patch grid in {max(1, (side + 1) // 2)} x {max(1, (side + 1) // 2)} local windows"
 
     # NC-SSD on inputs of the same shape: x, B, C in the io dtype, m fp32
@@ -270,11 +278,11 @@ def main(argv=None):
     nc_base = {k: torch.from_numpy(nci[k]).to(dev) for k in ("x", "B", "C", "m")}
     for k in ("x", "B", "C"):
         nc_base[k] = nc_base[k].to(tdt)
-    calls["ncssd"] = []
-    for i in range(nc_copies):
-        t = {k: v.clone() for k, v in nc_base.items()}
-        calls["ncssd"].append(binding.PreparedNcssd(t["x"], t["B"], t["C"], t["m"], seg_len=w.seg_len,
-                                                    out=torch.empty_like(t["x"])))
+    nc_in = [{k: v.clone() for k, v in nc_base.items()} for _ in range(nc_copies)]
+    nc_out = [torch.empty_like(t["x"]) for t in nc_in]
+    mk["ncssd"] = lambda i, st=None: binding.PreparedNcssd(nc_in[i]["x"], nc_in[i]["B"], nc_in[i]["C"], nc_in[i]["m"],
+                                                           seg_len=w.seg_len, out=nc_out[i], stream=st)
+    calls["ncssd"] = [mk["ncssd"](i) for i in range(nc_copies)]
 
     stream = torch.cuda.current_stream(dev)
 
@@ -351,6 +359,12 @@ def main(argv=None):
         torch.cuda.synchronize(dev)
         return time.perf_counter() - t0
 
+    def leg_wall(name, eager_wall, n=ncopy):
+        """A leg's wall time for its `value`: its calls replayed from HIP graphs, like the headline
+        steps (eager calls' wall time with --no-graph)."""
+        return eager_wall if args.no_graph else graph_wall(mk[name], ncopy=n)
+    leg_launch = "eager library calls" if args.no_graph else "HIP graph replays of the whole call"
+
     if not args.no_graph:
         # The headline steps: the whole call replayed from HIP graphs, so the host's per-call
         # launch work is not on the GPU's critical path.
@@ -401,7 +415,8 @@ def main(argv=None):
         wall_g, per_call_g, per_scan_g = timed(True)
         kg = float(np.mean(per_scan_g))
         ops_g = alu_ops_per_element(False) * w.tokens_channels
-        out["general_decay"] = {"value": round(nbytes * args.steps / wall_g / 1e9, 2), "unit": "GB/s",
+        out["general_decay"] = {"value": round(nbytes * args.steps / leg_wall(True, wall_g) / 1e9, 2), "unit": "GB/s",
+                                "launch": leg_launch,
                                 "call_us": stats_us(per_call_g), "kernel_us": round(kg * 1e6, 3),
                                 "alu_achieved_tops": round(ops_g / kg / 1e12, 3),
                                 "alu_frac": round(ops_g / kg / 1e12 / VALU_PEAK_TOPS, 4),
@@ -414,7 +429,8 @@ def main(argv=None):
         # second skip-term FMA instead of the shared one
         ops_c = (alu_ops_per_element(geometric) + 2 * (4 + 3 + TRANS_OPS * 2) + 1) * w.tokens_channels
         out["conv_fused"] = {"what": "directional depthwise conv1d (4 taps) + SiLU fused in front of both scans",
-                             "value": round(cbytes * args.steps / wall_c / 1e9, 2), "unit": "GB/s",
+                             "value": round(cbytes * args.steps / leg_wall("conv", wall_c) / 1e9, 2), "unit": "GB/s",
+                             "launch": leg_launch,
                              "call_us": stats_us(per_call_c), "kernel_us": round(kc * 1e6, 3),
                              "alu_achieved_tops": round(ops_c / kc / 1e12, 3),
                              "alu_frac": round(ops_c / kc / 1e12 / VALU_PEAK_TOPS, 4)}
@@ -428,7 +444,8 @@ def main(argv=None):
             kf = float(np.mean(per_scan_f))
             out[label] = {"what": "forward scan alone (vimscan_fwd)" + (", with the auxiliary-token swap"
                                                                          if name == "fwd_swap" else ""),
-                          "value": round(fbytes * args.steps / wall_f / 1e9, 2), "unit": "GB/s",
+                          "value": round(fbytes * args.steps / leg_wall(name, wall_f) / 1e9, 2), "unit": "GB/s",
+                          "launch": leg_launch,
                           "call_us": stats_us(per_call_f), "kernel_us": round(kf * 1e6, 3),
                           "alu_achieved_tops": round(ops_f / kf / 1e12, 3),
                           "alu_frac": round(ops_f / kf / 1e12 / VALU_PEAK_TOPS, 4),
@@ -438,12 +455,14 @@ def main(argv=None):
         ko = float(np.mean(per_scan_o))
         obytes = nbytes + w.batch * w.seqlen * 4   # plus the order
         out["ordered"] = {"what": "the same scan in a given token order (vimscan_bidir_order_fwd): " + order_desc,
-                          "value": round(obytes * args.steps / wall_o / 1e9, 2), "unit": "GB/s",
+                          "value": round(obytes * args.steps / leg_wall("order", wall_o) / 1e9, 2), "unit": "GB/s",
+                          "launch": leg_launch,
                           "call_us": stats_us(per_call_o), "kernel_us": round(ko * 1e6, 3),
                           "alu_achieved_tops": round(ops / ko / 1e12, 3),
                           "alu_frac": round(ops / ko / 1e12 / VALU_PEAK_TOPS, 4)}
     if not args.no_ncssd:
-        out["ncssd"] = ncssd_leg(w, timed, stats_us, calls["ncssd"][0].plan, nc_bytes, nc_copies)
+        out["ncssd"] = ncssd_leg(w, timed, stats_us, calls["ncssd"][0].plan, nc_bytes, nc_copies,
+                                 value_wall=lambda eager: leg_wall("ncssd", eager, nc_copies), launch=leg_launch)
     if not args.no_copy:
         # measured HBM ceiling: a device copy of 512 MiB (read + write 1 GiB), outside the Infinity Cache
         n = 512 * 2 ** 20
