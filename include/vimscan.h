@@ -95,8 +95,9 @@ typedef struct vimscan_launch {
     int64_t d_state;        /* N; 16 for the scans; 16, 32 or 64 for vimscan_ncssd_fwd */
     int32_t io_dtype;       /* enum vimscan_io_dtype */
     int32_t flags;          /* VIMSCAN_FLAG_* bits */
-    int64_t chunk_len;      /* 0: the library picks; > 0: tokens per chunk of the chunked scan
-                               (values >= the sequence length give a single pass) */
+    int64_t chunk_len;      /* 0: the library picks; > 0: tokens per chunk of the chunked scan,
+                               capped at 256 (a value >= the sequence length gives a single
+                               pass for sequences of up to 256 tokens) */
     void* workspace;        /* device scratch of at least vimscan_workspace_bytes() bytes;
                                may be NULL when that size is 0 */
     size_t workspace_bytes; /* size of workspace */
