@@ -80,15 +80,22 @@ __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float v) { return __builtin_amdgcn_logf(v); }
 __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
 
-// softplus(v) * log2(e) = log2(1 + 2^(v log2 e)). The scan keeps delta in these log2 units: the
-// transitions are then 2^(A * delta2) with A as given, and the conversion back to natural units
-// is folded into the C rows (C * ln 2, applied once when they are staged). Above v = 20 the
-// correction log2(1 + 2^-(v log2 e)) < 3e-9 and v log2 e is returned.
-// Takes dt and bias * log2(e), so v * log2(e) is one fma.
+// softplus(v) * log2(e) = log2(1 + 2^w), w = v log2 e. The scan keeps delta in these log2 units:
+// the transitions are then 2^(A * delta2) with A as given, and the conversion back to natural
+// units is folded into the C rows (C * ln 2, applied once when they are staged).
+// Evaluated as max(w, 0) + log2(1 + p), p = 2^-|w| in (0, 1], which never forms 2^w for large w
+// (no overflow, no threshold test). log2(1 + p) is taken as log2(v) + r log2(e), v = 1 + p rounded
+// and r = p - (v - 1) its rounding error (exact): the correction is log2(1 + r / v) to first
+// order, with 1/v dropped, which costs at most 2^-24.5 of the result (log2(1 + p) >= p on (0, 1]).
+// Without it, log2(fl(1 + p)) alone is off by up to 2^-24 / p relative: 1e-4 at delta = 6e-4,
+// and 0 below delta = 6e-8 -- visible wherever one token's delta * x dominates the state.
+// Takes dt and bias * log2(e), so w is one fma.
 __device__ __forceinline__ float softplus_log2(float dt, float bias2) {
-    const float vl = fmaf(dt, kLog2e, bias2);
-    const float r = fast_log2(1.0f + fast_exp2(vl));
-    return vl > 20.0f * kLog2e ? vl : r;
+    const float w = fmaf(dt, kLog2e, bias2);
+    const float p = fast_exp2(-fabsf(w));
+    const float v = 1.0f + p;
+    const float r = p - (v - 1.0f);
+    return fmaxf(w, 0.0f) + fmaf(r, kLog2e, fast_log2(v));
 }
 
 // silu(v) = v / (1 + e^-v)
@@ -254,12 +261,18 @@ struct Lane {
 
     // The transition form this wave uses: one form for all 64 lanes (a wave-wide vote).
     // Also keeps A[d, 0] and A[d, 1] - A[d, 0] for the progression forms.
+    // The factored forms take only rows that are non-positive and non-increasing (A0 <= 0,
+    // dA <= 0): then e0 = 2^(delta2 A0) is the largest transition and at most 1, q <= 1, and
+    // e0 q^n can underflow only where the exact transition is itself below the smallest normal
+    // float. An ascending row would start the chain at its smallest transition, which underflows
+    // to 0 (or meets q = inf) while the later ones are still large; such rows take the general
+    // form.
     __device__ __forceinline__ int decay_form(const ScanArgs& a, int dir, int dc) {
         const float* A = a.A[dir] + dc * kN;
         a0 = A[0];
         da = A[1] - A[0];
         if (a.general) return kGeneral;
-        if (!__all(is_progression(a, dir, dc))) return kGeneral;
+        if (!__all(is_progression(a, dir, dc) && a0 <= 0.0f && da <= 0.0f)) return kGeneral;
         return __all(a0 == da) ? kGeometric : kProgression;
     }
 

@@ -1,6 +1,6 @@
 """Parity of the NC-SSD global-state form (vimscan_ncssd_fwd) with the float64 oracle, on the GPU,
 through the C ABI. Tolerances as for the scan: fp32 |y - y_ref| <= 1e-4 (1 + |y_ref|); bf16
-|y - y_ref| <= 2e-2 (|y_ref| + rms(y_ref)). Inputs from the seeded NC-SSD recipe: x, B, C ~ N(0, 1),
+|y - y_ref| <= 2e-2 max(|y_ref|, 0.1 rms(y_ref)). Inputs from the seeded NC-SSD recipe: x, B, C ~ N(0, 1),
 token weights m in (1, e]."""
 import numpy as np
 import pytest
