@@ -39,6 +39,7 @@ FP32_VECTOR_TFLOPS = 157.3    # MI355X fp32 vector peak, published: packed FMA, 
 # 256 CU x 64 lanes x 2.4 GHz lane-operations per second.
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 CACHE_BYTES = 256 * 2 ** 20   # Infinity Cache
+SETTLE_S = 0.15               # untimed device work before every leg's warm-up (clock ramp)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_vim_s.json")
 KERNEL_SOURCE = os.path.join(ROOT, "bidirectional_selective_scan_amd", "csrc", "vimscan.hip")
 NCSSD_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_ncssd_vim_s.json")
@@ -101,14 +102,7 @@ def cpu_model() -> str:
 
 def cpu_baseline(inp: dict, w) -> dict:
     import oracle
-    oracle.build(force=False)
-    x64 = {k: np.asarray(v, dtype=np.float64) for k, v in inp.items()}
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        oracle.bidir_fwd(x64, seg_len=w.seg_len)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
+    t = oracle_seconds(inp, w.seg_len)
     cores = oracle.max_threads()
     return {"value": round(w.algorithmic_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "seconds": round(t, 4), "cpu": cpu_model(),
@@ -139,10 +133,26 @@ def ncssd_leg(w, timed, stats_us, plan, nbytes, ncopies, value_wall=None, launch
                               "(high and low parts of B*m and H)"}}
 
 
-def configs_leg(graph_wall, dev, steps):
+def oracle_seconds(inp_np: dict, seg_len: int, runs: int = 3) -> float:
+    """Median wall time of the float64 oracle on one input set (host cores)."""
+    import oracle
+    oracle.build(force=False)
+    x64 = {k: np.asarray(v, dtype=np.float64) for k, v in inp_np.items()}
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.bidir_fwd(x64, seg_len=seg_len)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times))
+
+
+def configs_leg(graph_wall, dev, steps, headline=None, with_cpu=True):
     """Every workload at its full size (tiny, Vim-Ti, Vim-S, high-res, folded), timed as HIP graph
     replays of the whole library call with the plan's own chunking, on inputs drawn on the device
-    with the same distributions; rotating input copies past the Infinity Cache (at most 64)."""
+    with the same distributions; rotating input copies past the Infinity Cache (at most 64). The
+    headline workload's entry is the headline measurement itself (headline = (name, seconds per
+    step)), so the line holds one number for it. With with_cpu, the float64 oracle is timed on each
+    workload's inputs (median of 3 runs on the host's cores)."""
     import torch
     from bidirectional_selective_scan_amd import binding
     from bidirectional_selective_scan_amd.configs import WORKLOADS
@@ -153,22 +163,39 @@ def configs_leg(graph_wall, dev, steps):
     for w in WORKLOADS:
         inp = device_inputs(w.batch, w.seqlen, w.d_inner, 16, w.io_dtype, seed=0, device=str(dev))
         nbytes = w.algorithmic_bytes()
-        n = min(64, max(2, -(-2 * CACHE_BYTES // nbytes) + 1))
-        copies = [[inp[k].clone() for k in io_names] for _ in range(n)]
-        outs = [torch.empty_like(inp["x"]) for _ in range(n)]
-        params = [inp[k] for k in par_names]
         plan = binding.launch_info(w.batch, w.seqlen, w.d_inner, 16, w.seg_len, w.io_dtype)
-        ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
-        wall = graph_wall(lambda i, s: binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i],
-                                                            workspace=ws, stream=s), ncopy=n, warmup=200)
-        step = wall / steps
+        if headline is not None and headline[0] == w.name:
+            step = headline[1]
+            source = "the headline measurement"
+        else:
+            n = min(64, max(2, -(-2 * CACHE_BYTES // nbytes) + 1))
+            copies = [[inp[k].clone() for k in io_names] for _ in range(n)]
+            outs = [torch.empty_like(inp["x"]) for _ in range(n)]
+            params = [inp[k] for k in par_names]
+            ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+            wall = graph_wall(lambda i, s: binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i],
+                                                                workspace=ws, stream=s), ncopy=n)
+            step = wall / steps
+            source = f"HIP graph replays of the whole call, {n} rotating input copies"
+            del copies, outs, ws
         ops = alu_ops_per_element(True) * w.tokens_channels
         res[w.name] = {"us_per_call": round(step * 1e6, 3), "gbs": round(nbytes / step / 1e9, 2),
                        "pct_hbm_peak": round(100 * nbytes / step / 1e9 / HBM_PEAK_GBS, 2),
                        "tokens_channels_per_s": round(w.tokens_channels / step, 1),
                        "alu_frac": round(ops / step / 1e12 / VALU_PEAK_TOPS, 4),
+                       "source": source,
                        "plan": {k: plan[k] for k in ("chunk_len", "chunks", "workgroups", "kernels")}}
-        del copies, outs, inp, ws
+        if with_cpu:
+            host = {k: (v.float().cpu().numpy() if v.dtype != torch.float32 else v.cpu().numpy())
+                    for k, v in inp.items()}
+            import oracle
+            t = oracle_seconds(host, w.seg_len)
+            res[w.name]["cpu"] = {"seconds": round(t, 4), "cores": oracle.max_threads(),
+                                  "gbs": round(nbytes / t / 1e9, 4),
+                                  "tokens_channels_per_s": round(w.tokens_channels / t, 1),
+                                  "kind": "oracle (float64, median of 3)"}
+            del host
+        del inp
     return res
 
 
@@ -176,9 +203,11 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # Untimed calls before every leg. The GPU needs tens of milliseconds of continuous work to
-    # reach its steady clocks: after 10 calls the Vim-S step measured ~125 us, after 500 ~101 us.
-    ap.add_argument("--warmup", type=int, default=500)
+    # Untimed calls before every leg's timed steps. Each leg first runs the same call untimed for
+    # SETTLE_S seconds (the GPU needs tens of milliseconds of continuous work to reach its steady
+    # clocks: after 10 calls from idle the Vim-S step measured ~125 us, after 500 ~101 us), then
+    # the W warm-up calls, then the K timed steps.
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="workload name (default: Vim-S)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-general", action="store_true", help="skip the forced general-decay measurement")
@@ -294,9 +323,21 @@ def main(argv=None):
         torch.cuda.synchronize(dev)
         return evs
 
+    def settle(run_one):
+        """Untimed calls for SETTLE_S seconds of wall time (at least 20), then a synchronize."""
+        t_end = time.perf_counter() + SETTLE_S
+        i = 0
+        while i < 20 or time.perf_counter() < t_end:
+            run_one(i)
+            i += 1
+            if i % 20 == 0:
+                torch.cuda.synchronize(dev)
+        torch.cuda.synchronize(dev)
+
     def timed(which):   # False: automatic transitions, True: forced general, "conv": with the convolution
         cl = calls[which]
         ncopy = len(cl)
+        settle(lambda i: cl[i % ncopy]())
         for i in range(args.warmup):
             cl[i % ncopy]()
         torch.cuda.synchronize(dev)
@@ -348,6 +389,7 @@ def main(argv=None):
             return g
         block = capture(range(ncopy))
         singles = [capture([i]) for i in range(ncopy)]
+        settle(lambda i: singles[i % ncopy].replay())
         for i in range(warmup):
             singles[i % ncopy].replay()
         torch.cuda.synchronize(dev)
@@ -379,6 +421,7 @@ def main(argv=None):
     ops = alu_ops_per_element(geometric) * w.tokens_channels
     alu_tops = ops / kernel_s / 1e12
     traffic = load_traffic(w.name)
+    hbm_gbs = nbytes / kernel_s / 1e9
     out = {
         "metric": "bidirectional selective-scan GB/s & % HBM peak at Vim-S shape (B128,L197,Di768)",
         "value": round(value, 2),
@@ -390,26 +433,35 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # x, dt, z, B, C and y are stored in the workload's io dtype; state, transitions and every
+        # sum are fp32
+        "dtype": w.io_dtype,
+        "state_dtype": "f32",
         "data": "synthetic",
         "config": {**w.describe(), "chunks": plan["chunks"], "kernels_per_step": plan["kernels"],
-                   "input_copies": ncopy, "launch": launch_mode},
+                   "input_copies": ncopy, "launch": launch_mode,
+                   "clock_policy": f"every leg runs its call untimed for {SETTLE_S} s, then the {args.warmup} "
+                                   f"warm-up calls, then the timed steps"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "call_us": stats_us(per_call),
         "kernel_us": round(kernel_s * 1e6, 3),
         "scan_kernel_us": stats_us(per_scan),
-        "kernel_gbs": round(nbytes / kernel_s / 1e9, 2),
+        "kernel_gbs": round(hbm_gbs, 2),
         "tokens_channels_per_s": round(w.tokens_channels / kernel_s, 1),
-        "roofline": {"bound": "alu", "achieved": round(alu_tops, 3), "peak": round(VALU_PEAK_TOPS, 3),
-                     "unit": "Top/s", "frac": round(alu_tops / VALU_PEAK_TOPS, 4), "traffic": traffic,
-                     "kernel": "k_bidir_scan",
-                     "ops_per_element": alu_ops_per_element(geometric),
-                     "peak_basis": "fp32 VALU lane-operations per second without packed instructions "
-                                   "(256 CU x 64 lanes x 2.4 GHz); a transcendental counts 2",
-                     # against the packed-instruction issue rate behind the published 157.3 TFLOP/s
-                     "frac_of_packed_peak": round(alu_tops / (2 * VALU_PEAK_TOPS), 4),
-                     "hbm": {"achieved": round(nbytes / kernel_s / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(nbytes / kernel_s / 1e9 / HBM_PEAK_GBS, 4)}},
+        # The metric's roofline: algorithmic bytes per launch of the dominant kernel (the scan) over
+        # its mean duration between the HIP events the library records around it on its stream.
+        "roofline": {"bound": "hbm", "achieved": round(hbm_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "k_bidir_scan", "algorithmic_bytes": nbytes,
+                     # What binds the scan: the fp32 vector ALU (its lane-operation rate).
+                     "binding": "alu",
+                     "alu": {"achieved": round(alu_tops, 3), "peak": round(VALU_PEAK_TOPS, 3), "unit": "Top/s",
+                             "frac": round(alu_tops / VALU_PEAK_TOPS, 4),
+                             "ops_per_element": alu_ops_per_element(geometric),
+                             "peak_basis": "fp32 VALU lane-operations per second without packed instructions "
+                                           "(256 CU x 64 lanes x 2.4 GHz); a transcendental counts 2",
+                             # against the packed-instruction issue rate behind the published 157.3 TFLOP/s
+                             "frac_of_packed_peak": round(alu_tops / (2 * VALU_PEAK_TOPS), 4)}},
     }
     if not args.no_general:
         wall_g, per_call_g, per_scan_g = timed(True)
@@ -478,8 +530,8 @@ def main(argv=None):
         torch.cuda.synchronize(dev)
         ceil_gbs = 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
-        out["roofline"]["hbm"]["copy_ceiling"] = round(ceil_gbs, 1)
-        out["roofline"]["hbm"]["frac_of_copy"] = round(nbytes / kernel_s / 1e9 / ceil_gbs, 4)
+        out["roofline"]["copy_ceiling"] = round(ceil_gbs, 1)
+        out["roofline"]["frac_of_copy"] = round(nbytes / kernel_s / 1e9 / ceil_gbs, 4)
         if "ncssd" in out:
             out["ncssd"]["roofline"]["copy_ceiling"] = round(ceil_gbs, 1)
             out["ncssd"]["roofline"]["frac_of_copy"] = round(out["ncssd"]["roofline"]["achieved"] / ceil_gbs, 4)
@@ -510,7 +562,8 @@ def main(argv=None):
                                "alu_frac_step": round(ops / 8 / step_s / 1e12 / VALU_PEAK_TOPS, 4),
                                "plan": {k: plan_s[k] for k in ("chunks", "workgroups", "park_in_workspace")}}
     if not args.no_configs and not args.no_graph:
-        out["configs"] = configs_leg(graph_wall, dev, args.steps)
+        out["configs"] = configs_leg(graph_wall, dev, args.steps, headline=(w.name, wall / args.steps),
+                                     with_cpu=not args.no_cpu)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, w)
     print(json.dumps(out), flush=True)
