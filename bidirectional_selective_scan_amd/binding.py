@@ -50,7 +50,10 @@ class _Conv(ctypes.Structure):
 
 EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_fwd", "vimscan_plan_launch",
             "vimscan_workspace_bytes", "vimscan_status_string", "vimscan_version", "vimscan_ncssd_fwd",
-            "vimscan_ncssd_plan", "vimscan_bidir_order_fwd")
+            "vimscan_ncssd_plan", "vimscan_bidir_order_fwd", "vimscan_bidir_fwd_noalloc")
+
+# Size of the static scratch array behind vimscan_bidir_fwd_noalloc (VIMSCAN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def lib_path() -> str:
@@ -69,6 +72,8 @@ def load_library():
             vp = ctypes.c_void_p
             lib.vimscan_bidir_fwd.restype = ctypes.c_int
             lib.vimscan_bidir_fwd.argtypes = [vp] * 13 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
+            lib.vimscan_bidir_fwd_noalloc.restype = ctypes.c_int
+            lib.vimscan_bidir_fwd_noalloc.argtypes = [vp] * 13 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
             lib.vimscan_fwd.restype = ctypes.c_int
             lib.vimscan_fwd.argtypes = [vp] * 8 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
             lib.vimscan_bidir_conv_fwd.restype = ctypes.c_int
@@ -145,8 +150,11 @@ class PreparedCall:
 
     def __init__(self, x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
                  out=None, chunk_len: int = 0, general_decay: bool = False, workspace=None, stream=None,
-                 conv=None, aux_swap: bool = False, forward_only: bool = False, order=None):
+                 conv=None, aux_swap: bool = False, forward_only: bool = False, order=None, noalloc: bool = False):
         lib = load_library()
+        if noalloc and (conv is not None or forward_only or order is not None or aux_swap or workspace is not None):
+            raise ValueError("the allocation-free call is the plain bidirectional scan (no conv, order, swap, "
+                             "forward-only or workspace)")
         if forward_only and conv is not None:
             raise ValueError("the forward-only scan takes no convolution")
         if order is not None and (conv is not None or forward_only):
@@ -196,7 +204,7 @@ class PreparedCall:
                              forward_only=forward_only)
         need = ctypes.c_size_t(0)
         _check(lib.vimscan_workspace_bytes(ctypes.byref(launch), int(seg_len), ctypes.byref(need)))
-        if need.value > 0:
+        if need.value > 0 and not noalloc:
             if workspace is None or workspace.numel() * workspace.element_size() < need.value:
                 workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
             launch.workspace = workspace.data_ptr()
@@ -205,7 +213,11 @@ class PreparedCall:
         self._keep = (ios, params, out, workspace)   # keep every buffer alive while prepared
         self._launch = launch
         self._conv = cstruct
-        if forward_only:
+        if noalloc:
+            self._fn = lib.vimscan_bidir_fwd_noalloc
+            self._args = (tuple(t.data_ptr() for t in ios + params)
+                          + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
+        elif forward_only:
             self._fn = lib.vimscan_fwd
             self._args = (tuple(t.data_ptr() for t in (x, dt, z, B_f, C_f, A_f, D_f, dt_bias_f))
                           + (int(seg_len), out.data_ptr(), ctypes.byref(launch)))
@@ -231,6 +243,16 @@ class PreparedCall:
     def __call__(self):
         _check(self._fn(*self._args))
         return self.out
+
+
+def bidir_fwd_noalloc(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,
+                      out=None, chunk_len: int = 0, general_decay: bool = False):
+    """bidir_fwd through vimscan_bidir_fwd_noalloc: the library takes its scratch from its static
+    per-GPU array (at most NOALLOC_SCRATCH_BYTES) instead of a workspace. With ``out`` given the
+    call allocates no device memory at all. Queued on torch's current stream; does not
+    synchronise."""
+    return PreparedCall(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len, out,
+                        chunk_len, general_decay, noalloc=True)()
 
 
 def bidir_fwd(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, seg_len: int = 0,

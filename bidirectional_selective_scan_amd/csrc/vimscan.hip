@@ -53,6 +53,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "vimscan.h"
 
@@ -980,6 +981,7 @@ const char* const kStatusText[] = {
     "bad chunk_len: must be >= 0",
     "unknown flag bits",
     "bad convolution: k must be 1..4",
+    "the call needs more scratch than the allocation-free entry point's static array holds (96 MiB)",
 };
 
 int check_shape(const vimscan_launch* l, int64_t seg_len) {
@@ -1129,12 +1131,37 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
     return VIMSCAN_OK;
 }
 
+// Scratch of the allocation-free entry point (vimscan_bidir_fwd_noalloc): a static device array,
+// one copy per GPU the library runs on, held until the process ends. In host code the array's name
+// is not a device address; host code uses only the per-device address hipGetSymbolAddress gives.
+static_assert(VIMSCAN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[VIMSCAN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The current device's scratch address (looked up on the device's first use).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VIMSCAN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VIMSCAN_ERR_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return VIMSCAN_OK;
+}
+
 // Every entry point: conv is NULL without the convolution, order NULL in raster order (not both
-// set).
+// set). use_scratch: the workspace is the static scratch array (vimscan_bidir_fwd_noalloc), not
+// launch->workspace.
 int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, const void* C_f, const void* B_b,
                const void* C_b, const float* A_f, const float* A_b, const float* D_f, const float* D_b,
                const float* dt_bias_f, const float* dt_bias_b, const vimscan_conv* conv, const int32_t* order,
-               int64_t seg_len, void* y, const vimscan_launch* launch) {
+               int64_t seg_len, void* y, const vimscan_launch* launch, bool use_scratch = false) {
     if (!launch) return VIMSCAN_ERR_NULL;
     Plan p;
     int rc = make_plan(launch, seg_len, &p);
@@ -1180,7 +1207,8 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
         if (in.n && !aligned(in.p, 4)) return VIMSCAN_ERR_ALIGN;
         if (overlaps(y, S * e, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
     }
-    if (p.ws > 0) {
+    if (use_scratch && p.ws > VIMSCAN_NOALLOC_SCRATCH_BYTES) return VIMSCAN_ERR_SCRATCH;
+    if (p.ws > 0 && !use_scratch) {
         if (!launch->workspace || launch->workspace_bytes < p.ws) return VIMSCAN_ERR_WORKSPACE;
         if (!aligned(launch->workspace, 16)) return VIMSCAN_ERR_ALIGN;
         if (overlaps(y, S * e, launch->workspace, p.ws)) return VIMSCAN_ERR_ALIAS;
@@ -1206,6 +1234,12 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.dtb[1] = dt_bias_b;
     a.y = y;
     char* ws = static_cast<char*>(launch->workspace);
+    if (use_scratch && p.ws > 0) {  // every argument check has passed: the first HIP call
+        void* sp = nullptr;
+        rc = scratch_address(&sp);
+        if (rc != VIMSCAN_OK) return rc;
+        ws = static_cast<char*>(sp);
+    }
     a.carry = p.K > 1 ? reinterpret_cast<float*>(ws) : nullptr;
     a.dsum = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_dsum) : nullptr;
     a.parkg = p.park_global ? reinterpret_cast<float*>(ws + p.off_park) : nullptr;
@@ -1284,6 +1318,15 @@ int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* 
     if (launch && (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY)) return VIMSCAN_ERR_FLAGS;
     return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, nullptr, nullptr, seg_len, y,
                       launch);
+}
+
+int vimscan_bidir_fwd_noalloc(const void* x, const void* dt, const void* z, const void* B_f, const void* C_f,
+                              const void* B_b, const void* C_b, const float* A_f, const float* A_b, const float* D_f,
+                              const float* D_b, const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len,
+                              void* y, const vimscan_launch* launch) {
+    if (launch && (launch->flags & VIMSCAN_FLAG_FORWARD_ONLY)) return VIMSCAN_ERR_FLAGS;
+    return bidir_impl(x, dt, z, B_f, C_f, B_b, C_b, A_f, A_b, D_f, D_b, dt_bias_f, dt_bias_b, nullptr, nullptr, seg_len, y,
+                      launch, true);
 }
 
 int vimscan_fwd(const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,

@@ -66,7 +66,9 @@ enum vimscan_status {
     VIMSCAN_ERR_HIP = -8,       /* a kernel launch failed (hipGetLastError after launching) */
     VIMSCAN_ERR_CHUNK = -9,     /* chunk_len < 0 */
     VIMSCAN_ERR_FLAGS = -10,    /* unknown bits in flags */
-    VIMSCAN_ERR_CONV = -11      /* vimscan_conv.k outside 1..4 */
+    VIMSCAN_ERR_CONV = -11,     /* vimscan_conv.k outside 1..4 */
+    VIMSCAN_ERR_SCRATCH = -12   /* vimscan_bidir_fwd_noalloc: the call needs more scratch than
+                                   VIMSCAN_NOALLOC_SCRATCH_BYTES */
 };
 
 /* dtype of x, dt, z, B_*, C_* and y. */
@@ -245,6 +247,32 @@ int vimscan_ncssd_fwd(const void* x, const void* B, const void* C, const float* 
    it is: partial states, their sum, readout); workspace_bytes (0 when not split). Host only. Returns VIMSCAN_OK or the error the call would
    return. */
 int vimscan_ncssd_plan(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan);
+
+/* Size of the static scratch array behind vimscan_bidir_fwd_noalloc, per GPU: 96 MiB. */
+#define VIMSCAN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): vimscan_bidir_fwd with its scratch (the chunk carries,
+ * delta sums and long-chunk park that vimscan_workspace_bytes reports) taken from a static device
+ * array of VIMSCAN_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+ * process ends, instead of from launch->workspace (whose two fields are ignored). Arguments,
+ * results, plan and every other error are those of vimscan_bidir_fwd, checked in the same order
+ * before any HIP call; a call whose workspace_bytes exceed VIMSCAN_NOALLOC_SCRATCH_BYTES returns
+ * VIMSCAN_ERR_SCRATCH without launching (every workload shape of this library fits, Vim-S's
+ * 77.5 MB park included). The array belongs to the current HIP device: its address is looked up
+ * (hipGetSymbolAddress) on the first call on each device, which must therefore be current; the
+ * call allocates nothing (no hipMalloc, hipFree or allocating library routine). The array keeps
+ * the last call's contents; no part of the scan reads scratch it has not written in the same
+ * call. Calls on one GPU share its array: two calls that can overlap in time on the same GPU
+ * (different streams without an ordering between them) race on it and give undefined results;
+ * calls on one stream are ordered and safe.
+ */
+int vimscan_bidir_fwd_noalloc(const void* x, const void* dt, const void* z, const void* B_f,
+                              const void* C_f, const void* B_b, const void* C_b, const float* A_f,
+                              const float* A_b, const float* D_f, const float* D_b,
+                              const float* dt_bias_f, const float* dt_bias_b, int64_t seg_len, void* y,
+                              const vimscan_launch* launch);
 
 /* Fills *plan for a call with this launch and seg_len (workspace fields of launch are
    ignored). Host only; no HIP call. Returns VIMSCAN_OK or the error the call would return. */

@@ -14,8 +14,8 @@ from bidirectional_selective_scan_amd.configs import WORKLOADS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vimscan.h")
 
-OK, NULL, SHAPE, SEGLEN, DTYPE, ALIGN, ALIAS, WORKSPACE, HIP, CHUNK, FLAGS, CONV = (0, -1, -2, -3, -4, -5, -6, -7, -8,
-                                                                     -9, -10, -11)
+OK, NULL, SHAPE, SEGLEN, DTYPE, ALIGN, ALIAS, WORKSPACE, HIP, CHUNK, FLAGS, CONV, SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12)
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +41,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -12, -1):
+    for code in range(0, -13, -1):
         s = binding.status_string(code)
         assert s and s != "unknown status"
     assert binding.status_string(-99) == "unknown status"
@@ -193,6 +193,40 @@ def test_workspace_required_for_chunked_plans(lib):
     launch.workspace_bytes = need.value
     launch.workspace = 0x10000000 + 64       # overlaps x
     assert _call(lib, launch) == ALIAS
+
+
+def test_noalloc_entry_point_arguments(lib):
+    """vimscan_bidir_fwd_noalloc: the arguments of vimscan_bidir_fwd, checked the same way before
+    any HIP call; a plan whose scratch exceeds the static array is VIMSCAN_ERR_SCRATCH."""
+    ptrs = [0x10000000 * (i + 1) for i in range(13)]
+    y = 0x7F000000
+
+    def call(launch, p=ptrs, seg_len=0, yy=y):
+        return lib.vimscan_bidir_fwd_noalloc(*p, seg_len, yy, ctypes.byref(launch) if launch is not None else None)
+
+    assert call(None) == NULL
+    assert call(_launch(d_state=8)) == SHAPE
+    assert call(_launch(seqlen=12), seg_len=5) == SEGLEN
+    assert call(_launch(io_dtype=2)) == DTYPE
+    bad = list(ptrs)
+    bad[0] += 2
+    assert call(_launch(), bad) == ALIGN
+    assert call(_launch(), ptrs, yy=ptrs[0] + 256) == ALIAS
+    launch = _launch()
+    launch.flags = binding.VIMSCAN_FLAG_FORWARD_ONLY
+    assert call(launch) == FLAGS
+    assert call(_launch(batch=0), [0] * 13, yy=0) == OK   # empty: nothing launched
+    # Vim-S at batch 256: a 155 MB park, more than the 96 MiB array (x etc. spaced far apart)
+    big = _launch(batch=256, seqlen=197, d_inner=768, io_dtype=binding.VIMSCAN_BF16)
+    need = ctypes.c_size_t(0)
+    assert lib.vimscan_workspace_bytes(ctypes.byref(big), 0, ctypes.byref(need)) == OK
+    assert need.value > binding.NOALLOC_SCRATCH_BYTES
+    far = [0x100000000 * (i + 1) for i in range(13)]
+    assert call(big, far, yy=0x100000000 * 20) == SCRATCH
+    # the batch-128 workload fits
+    vim_s = _launch(batch=128, seqlen=197, d_inner=768, io_dtype=binding.VIMSCAN_BF16)
+    assert lib.vimscan_workspace_bytes(ctypes.byref(vim_s), 0, ctypes.byref(need)) == OK
+    assert 0 < need.value <= binding.NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_bytes_rejects_bad_shapes(lib):
