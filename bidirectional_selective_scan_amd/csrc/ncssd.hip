@@ -48,18 +48,20 @@
 #include <cstring>
 #include <type_traits>
 
+#include "plan.h"
 #include "vimscan.h"
 
 namespace {
 
+using vimscan_host::NcPlan;
+
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 16;        // tokens per MFMA tile
-constexpr int kBlock = 64;       // channels per workgroup
-constexpr int kWaves = 4;        // waves per workgroup
-constexpr int kOutTokens = 128;  // tokens per pass-2 workgroup
-constexpr int64_t kTargetWgs = 1024;
+constexpr int kTile = vimscan_host::kNcTile;          // tokens per MFMA tile
+constexpr int kBlock = vimscan_host::kNcBlock;        // channels per workgroup
+constexpr int kWaves = vimscan_host::kNcWaves;        // waves per workgroup
+constexpr int kOutTokens = vimscan_host::kNcOutTokens;  // tokens per pass-2 workgroup
 constexpr int kStageRow = 36;   // words per token row of a wave's bf16 output tile in LDS (32 + 4 pad)
 constexpr int kStageRowF = 68;  // the same for fp32 (64 + 4 pad)
 template <typename IO> constexpr int kStageWords = kTile * (sizeof(IO) == 2 ? kStageRow : kStageRowF);  // per wave
@@ -489,66 +491,6 @@ __global__ __launch_bounds__(256) void k_ncssd_out(NcArgs a) {
 // ---------------------------------------------------------------------------------------------
 // Host side
 
-struct NcPlan {
-    int64_t nseq, T, splits, span, ncb, groups, N;
-    size_t off_H, ws;
-};
-
-bool aligned(const void* p, uintptr_t al) { return (reinterpret_cast<uintptr_t>(p) % al) == 0; }
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return na > 0 && nb > 0 && a0 < b0 + nb && b0 < a0 + na;
-}
-
-int nc_plan(const vimscan_launch* l, int64_t seg_len, NcPlan* p) {
-    if (!l) return VIMSCAN_ERR_NULL;
-    if (l->batch < 0 || l->seqlen < 0 || l->d_inner < 0) return VIMSCAN_ERR_SHAPE;
-    if (l->d_state != 16 && l->d_state != 32 && l->d_state != 64) return VIMSCAN_ERR_SHAPE;
-    if (l->d_inner % 16 != 0 || l->d_inner >= (int64_t(1) << 22)) return VIMSCAN_ERR_SHAPE;
-    const int64_t lim = int64_t(1) << 31;
-    if (l->batch > 0 && l->seqlen > 0 && l->d_inner > 0) {
-        if (l->seqlen > lim / l->batch) return VIMSCAN_ERR_SHAPE;
-        const int64_t bl = l->batch * l->seqlen;
-        if (l->d_inner >= lim / bl + 1 || bl * l->d_inner >= lim) return VIMSCAN_ERR_SHAPE;
-    }
-    if (l->io_dtype != VIMSCAN_F32 && l->io_dtype != VIMSCAN_BF16) return VIMSCAN_ERR_DTYPE;
-    if (seg_len < 0 || (seg_len > 0 && l->seqlen % seg_len != 0)) return VIMSCAN_ERR_SEGLEN;
-    if (l->chunk_len < 0) return VIMSCAN_ERR_CHUNK;
-    if (l->flags != 0) return VIMSCAN_ERR_FLAGS;
-    std::memset(p, 0, sizeof(*p));
-    p->N = l->d_state;
-    if (l->batch == 0 || l->seqlen == 0 || l->d_inner == 0) return VIMSCAN_OK;
-    p->T = seg_len > 0 ? seg_len : l->seqlen;
-    p->nseq = l->batch * (l->seqlen / p->T);
-    p->ncb = (l->d_inner + kBlock - 1) / kBlock;
-    const int64_t quantum = kTile * kWaves;  // one tile per wave
-    int64_t span;
-    if (l->chunk_len > 0) {
-        span = (l->chunk_len + kTile - 1) / kTile * kTile;
-    } else {
-        // Split long sequences until the pass has about kTargetWgs workgroups, keeping at least
-        // two tiles per wave.
-        const int64_t wgs = p->nseq * p->ncb;
-        int64_t k = wgs >= kTargetWgs ? 1 : (kTargetWgs + wgs - 1) / wgs;
-        const int64_t kmax = (p->T + 2 * quantum - 1) / (2 * quantum);
-        if (k > kmax) k = kmax;
-        if (k < 1) k = 1;
-        span = (p->T + k - 1) / k;
-        span = (span + quantum - 1) / quantum * quantum;
-    }
-    if (span >= p->T) span = (p->T + kTile - 1) / kTile * kTile;
-    p->span = span;
-    p->splits = (p->T + span - 1) / span;
-    p->groups = (p->T + kOutTokens - 1) / kOutTokens;
-    if (p->splits > 1) {  // split partial states, then H
-        const size_t hsz = static_cast<size_t>(p->nseq) * p->N * l->d_inner * sizeof(float);
-        p->off_H = (hsz * static_cast<size_t>(p->splits) + 255) / 256 * 256;
-        p->ws = p->off_H + hsz;
-    }
-    return VIMSCAN_OK;
-}
-
 template <typename IO, int NB>
 int nc_launch(const NcArgs& a, const NcPlan& p, hipStream_t s) {
     const dim3 block(kBlock * kWaves);
@@ -577,49 +519,16 @@ int nc_dispatch(const NcArgs& a, const NcPlan& p, hipStream_t s) {
 
 extern "C" {
 
-int vimscan_ncssd_plan(const vimscan_launch* launch, int64_t seg_len, vimscan_plan* plan) {
-    if (!plan) return VIMSCAN_ERR_NULL;
-    NcPlan p;
-    const int rc = nc_plan(launch, seg_len, &p);
-    if (rc != VIMSCAN_OK) return rc;
-    plan->sequences = p.nseq;
-    plan->seq_tokens = p.T;
-    plan->chunk_len = p.span;
-    plan->chunks = p.splits;
-    plan->workgroups = p.nseq * p.ncb * p.splits;
-    plan->kernels = p.nseq == 0 ? 0 : (p.splits > 1 ? 3 : 1);
-    plan->park_in_workspace = 0;
-    plan->workspace_bytes = p.ws;
-    return VIMSCAN_OK;
-}
-
 int vimscan_ncssd_fwd(const void* x, const void* B, const void* C, const float* m, int64_t seg_len, void* y,
                       const vimscan_launch* launch) {
     if (!launch) return VIMSCAN_ERR_NULL;
     NcPlan p;
-    const int rc = nc_plan(launch, seg_len, &p);
+    int rc = vimscan_host::make_nc_plan(launch, seg_len, &p);
     if (rc != VIMSCAN_OK) return rc;
     if (launch->batch == 0 || launch->seqlen == 0 || launch->d_inner == 0) return VIMSCAN_OK;
-    if (!x || !B || !C || !m || !y) return VIMSCAN_ERR_NULL;
+    rc = vimscan_host::check_ncssd_call(x, B, C, m, y, launch, p);
+    if (rc != VIMSCAN_OK) return rc;
     const bool bf = launch->io_dtype == VIMSCAN_BF16;
-    const size_t e = bf ? 2 : 4;
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(B, e) || !aligned(C, bf ? 8 : 16) || !aligned(m, 4))
-        return VIMSCAN_ERR_ALIGN;
-    const size_t tokens = static_cast<size_t>(launch->batch) * launch->seqlen;
-    const size_t ny = tokens * launch->d_inner * e;
-    const struct {
-        const void* p;
-        size_t n;
-    } ins[] = {{x, ny}, {B, tokens * p.N * e}, {C, tokens * p.N * e}, {m, tokens * 4}};
-    for (const auto& in : ins)
-        if (overlaps(y, ny, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
-    if (p.ws > 0) {
-        if (!launch->workspace || launch->workspace_bytes < p.ws) return VIMSCAN_ERR_WORKSPACE;
-        if (!aligned(launch->workspace, 16)) return VIMSCAN_ERR_ALIGN;
-        if (overlaps(y, ny, launch->workspace, p.ws)) return VIMSCAN_ERR_ALIAS;
-        for (const auto& in : ins)
-            if (overlaps(launch->workspace, p.ws, in.p, in.n)) return VIMSCAN_ERR_ALIAS;
-    }
 
     NcArgs a;
     a.x = x;
