@@ -22,11 +22,12 @@ constexpr int64_t kCus = 256;
 constexpr int64_t kLdsPerCu = 160 * 1024;
 
 // Workgroups of a chunked scan pass that one CU holds at once. The register budget of the scan
-// kernels (about 150-160 VGPRs with bf16 io, 175-200 with fp32) allows 3 waves per SIMD with bf16
-// and 2 with fp32, one wave of each workgroup on each SIMD; the bidirectional kernel's LDS (rows,
-// the order and a park in LDS) can allow fewer.
+// kernels (150-161 VGPRs with either io dtype) allows 3 waves per SIMD, one wave of each
+// workgroup on each SIMD; the bidirectional kernel's LDS (rows, the order and a park in LDS) can
+// allow fewer.
 int64_t resident_wgs(const ScanPlan* p, int io_dtype, int64_t T) {
-    int64_t r = io_dtype == VIMSCAN_BF16 ? 3 : 2;
+    (void)io_dtype;
+    int64_t r = 3;
     if (!p->uni) {
         const bool lds_park = T * kWave * static_cast<int64_t>(sizeof(float)) <= kLdsParkMaxBytes;
         const int64_t bytes = (4 * T * kN + T + (lds_park ? p->subs * T * kWave : 0)) * sizeof(float);

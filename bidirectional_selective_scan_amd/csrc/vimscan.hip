@@ -138,7 +138,15 @@ __device__ __forceinline__ uint32_t ld_raw(float, __amdgpu_buffer_rsrc_t r, uint
 __device__ __forceinline__ uint32_t ld_raw(Bf16, __amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so) {
     return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0));
 }
-__device__ __forceinline__ float widen(float, uint32_t raw) { return __uint_as_float(raw); }
+// An fp32 ring value is copied into a register of its own when it is taken (as the bf16 shift
+// does): the ring slot is then free for the refill the same step issues, where reusing the value in
+// place would keep two generations of the ring live (about 30 more VGPRs, 2 waves per SIMD
+// instead of 3).
+__device__ __forceinline__ float widen(float, uint32_t raw) {
+    uint32_t v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(raw));
+    return __uint_as_float(v);
+}
 __device__ __forceinline__ float widen(Bf16, uint32_t raw) { return __uint_as_float(raw << 16); }
 __device__ __forceinline__ void st_buf(float, __amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
