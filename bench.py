@@ -208,6 +208,8 @@ def main(argv=None):
     # clocks: after 10 calls from idle the Vim-S step measured ~125 us, after 500 ~101 us), then
     # the W warm-up calls, then the K timed steps.
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed calls before each leg's warm-up (clock ramp; 0 for counter runs)")
     ap.add_argument("--workload", default=None, help="workload name (default: Vim-S)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-general", action="store_true", help="skip the forced general-decay measurement")
@@ -324,8 +326,11 @@ def main(argv=None):
         return evs
 
     def settle(run_one):
-        """Untimed calls for SETTLE_S seconds of wall time (at least 20), then a synchronize."""
-        t_end = time.perf_counter() + SETTLE_S
+        """Untimed calls for args.settle seconds of wall time (at least 20 calls unless it is 0),
+        then a synchronize."""
+        if args.settle <= 0:
+            return
+        t_end = time.perf_counter() + args.settle
         i = 0
         while i < 20 or time.perf_counter() < t_end:
             run_one(i)
@@ -440,7 +445,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {**w.describe(), "chunks": plan["chunks"], "kernels_per_step": plan["kernels"],
                    "input_copies": ncopy, "launch": launch_mode,
-                   "clock_policy": f"every leg runs its call untimed for {SETTLE_S} s, then the {args.warmup} "
+                   "clock_policy": f"every leg runs its call untimed for {args.settle} s, then the {args.warmup} "
                                    f"warm-up calls, then the timed steps"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "call_us": stats_us(per_call),

@@ -255,34 +255,36 @@ struct Lane {
         cbias = a.cb[dir][dc];
     }
 
-    // True when A[d, :] is exactly A0 + n*(A1 - A0) in fp32. The row is read whole, before any
-    // comparison (one memory round trip, no chain of loads behind branches).
-    __device__ __forceinline__ bool is_progression(const ScanArgs& a, int dir, int dc) const {
-        const float* A = a.A[dir] + dc * kN;  // 4-byte aligned only
+    // The A row the transition-form vote reads, loaded whole (one memory round trip, no chain of
+    // loads behind branches); the kernels issue it before the row staging, so its latency
+    // overlaps the staging's.
+    struct ARow {
         float r[kN];
+    };
+    __device__ __forceinline__ ARow load_arow(const ScanArgs& a, int dir, int dc) const {
+        ARow row;
+        const float* A = a.A[dir] + dc * kN;  // 4-byte aligned only
 #pragma unroll
-        for (int n = 0; n < kN; ++n) r[n] = A[n];
-        const float s = r[1] - r[0];
-        bool ok = true;
-#pragma unroll
-        for (int n = 0; n < kN; ++n) ok &= (r[n] == r[0] + static_cast<float>(n) * s);
-        return ok;
+        for (int n = 0; n < kN; ++n) row.r[n] = A[n];
+        return row;
     }
 
-    // The transition form this wave uses: one form for all 64 lanes (a wave-wide vote).
-    // Also keeps A[d, 0] and A[d, 1] - A[d, 0] for the progression forms.
-    // The factored forms take only rows that are non-positive and non-increasing (A0 <= 0,
-    // dA <= 0): then e0 = 2^(delta2 A0) is the largest transition and at most 1, q <= 1, and
-    // e0 q^n can underflow only where the exact transition is itself below the smallest normal
-    // float. An ascending row would start the chain at its smallest transition, which underflows
-    // to 0 (or meets q = inf) while the later ones are still large; such rows take the general
-    // form.
-    __device__ __forceinline__ int decay_form(const ScanArgs& a, int dir, int dc) {
-        const float* A = a.A[dir] + dc * kN;
-        a0 = A[0];
-        da = A[1] - A[0];
+    // The transition form this wave uses: one form for all 64 lanes (a wave-wide vote). Keeps
+    // A[d, 0] and A[d, 1] - A[d, 0] for the progression forms.
+    // The factored forms take only rows that are exact arithmetic progressions in fp32 (A[n] ==
+    // A0 + n*dA) and non-positive and non-increasing (A0 <= 0, dA <= 0): then e0 = 2^(delta2 A0)
+    // is the largest transition and at most 1, q <= 1, and e0 q^n can underflow only where the
+    // exact transition is itself below the smallest normal float. An ascending row would start the
+    // chain at its smallest transition, which underflows to 0 (or meets q = inf) while the later
+    // ones are still large; such rows take the general form.
+    __device__ __forceinline__ int decay_form(const ScanArgs& a, const ARow& row) {
+        a0 = row.r[0];
+        da = row.r[1] - row.r[0];
         if (a.general) return kGeneral;
-        if (!__all(is_progression(a, dir, dc) && a0 <= 0.0f && da <= 0.0f)) return kGeneral;
+        bool ok = a0 <= 0.0f && da <= 0.0f;
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ok &= (row.r[n] == row.r[0] + static_cast<float>(n) * da);
+        if (!__all(ok)) return kGeneral;
         return __all(a0 == da) ? kGeometric : kProgression;
     }
 
@@ -374,6 +376,19 @@ enum WalkMode {
     kOut = 3        // forward only: gate and store every token (no park, no other direction)
 };
 
+// The register rings of a walk (see walk): raw x and dt of the steps ahead, z and the parked
+// output of the steps it gates, and in a given order the tokens they hold.
+constexpr int ring_depth(int var) { return var == kWithConv ? 5 : 6; }
+template <int P> struct Ring {
+    uint32_t xr[P], dr[P], zr[P], pr[P];
+    int tx[P], tz[P];
+};
+
+// How a walk treats its rings: fill them and run (kRingFull); only fill them and return
+// (kRingPrime: the kernels issue the first walk's ring loads before the row staging, whose latency
+// they then share); run on rings already filled (kRingPrimed).
+enum RingMode { kRingFull = 0, kRingPrime = 1, kRingPrimed = 2 };
+
 // x of one token by its raw bits (bf16 zero-extended), from the full tensor.
 template <typename IO>
 __device__ __forceinline__ uint32_t ld_global_raw(const void* base, int64_t i) {
@@ -392,13 +407,14 @@ __device__ __forceinline__ uint32_t ld_global_raw(const void* base, int64_t i) {
 // the three before it in walk order (a register window; at the walk's first step the window is
 // loaded from the tokens before it, which may lie in the neighbouring chunk, and is zero
 // outside the sequence).
-template <typename IO, int kDecay, int kMode, bool kGlobalPark, int kVar>
+template <typename IO, int kDecay, int kMode, bool kGlobalPark, int kVar, int kRing = kRingFull>
 __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
                                      const float* lds_c, const float* lds_b, const int32_t* lds_ord, int kbeg,
-                                     int kend, float& dsum) {
+                                     int kend, float& dsum, Ring<ring_depth(kVar)>& rg) {
     constexpr bool kConv = kVar == kWithConv;
     constexpr bool kOrd = kVar == kOrdered;
-    constexpr int P = kConv ? 5 : 6;  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
+    static_assert(!(kOrd && kRing != kRingFull), "an ordered walk's tokens come from LDS: it fills its own rings");
+    constexpr int P = ring_depth(kVar);  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
     constexpr uint32_t e = IoTraits<IO>::bytes;
     constexpr bool kReadout = kMode != kAggregate;
     using E = typename IoTraits<IO>::elem;
@@ -445,6 +461,39 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lt(min(k, last)))) * (kWave * 4);
     };
 
+    auto tokoff = [&](int t) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(t)) * rowb; };
+    // In a given order each step's token is looked up once, when its x and dt are requested, and
+    // rides along the rings: tx[s] is the token whose x/dt slot s holds, tz[s] the one whose z
+    // slot s holds (its y store offset). At the start of step kbeg + r, slot (r + i) % P of tx
+    // holds step kbeg + r + i (i = 1..P-1) and slot r % P step kbeg + r + P.
+    uint32_t (&xr)[P] = rg.xr;
+    uint32_t (&dr)[P] = rg.dr;
+    uint32_t (&zr)[P] = rg.zr;
+    uint32_t (&pr)[P] = rg.pr;
+    int (&tx)[P] = rg.tx;
+    int (&tz)[P] = rg.tz;
+    if constexpr (kRing != kRingPrimed) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            uint32_t so;
+            if constexpr (kOrd) {
+                tx[j] = tz[j] = trow(kbeg + j);
+                so = tokoff(tx[j]);
+            } else {
+                so = toff(kbeg + j);
+            }
+            xr[j] = ld_raw(IO{}, rx, vo, so);
+            dr[j] = ld_raw(IO{}, rd, vo, so);
+            if (kMode == kFinish || kMode == kOut) {
+                zr[j] = ld_raw(IO{}, rz, vo, so);
+                pr[j] = (kMode == kFinish && kGlobalPark)
+                            ? __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kbeg + j), 0)
+                            : 0u;
+            }
+        }
+    }
+    if constexpr (kRing == kRingPrime) return;
+
     Rates<kDecay> rates;
     rates.load(a.A[c.dir] + c.dc * kN, ln.a0, ln.da);
     float xw[kMaxTaps - 1];  // raw x (widened) of walk steps k-1, k-2, k-3
@@ -468,30 +517,6 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         return silu(acc);
     };
 
-    uint32_t xr[P], dr[P], zr[P], pr[P];
-    // In a given order each step's token is looked up once, when its x and dt are requested, and
-    // rides along the rings: tx[s] is the token whose x/dt slot s holds, tz[s] the one whose z
-    // slot s holds (its y store offset). At the start of step kbeg + r, slot (r + i) % P of tx
-    // holds step kbeg + r + i (i = 1..P-1) and slot r % P step kbeg + r + P.
-    int tx[P], tz[P];
-    auto tokoff = [&](int t) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(t)) * rowb; };
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        uint32_t so;
-        if constexpr (kOrd) {
-            tx[j] = tz[j] = trow(kbeg + j);
-            so = tokoff(tx[j]);
-        } else {
-            so = toff(kbeg + j);
-        }
-        xr[j] = ld_raw(IO{}, rx, vo, so);
-        dr[j] = ld_raw(IO{}, rd, vo, so);
-        if (kMode == kFinish || kMode == kOut) {
-            zr[j] = ld_raw(IO{}, rz, vo, so);
-            pr[j] = (kMode == kFinish && kGlobalPark) ? __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kbeg + j), 0)
-                                                      : 0u;
-        }
-    }
     // B and C rows come from the chunk's copy in LDS (staged once per workgroup), read as
     // wave-uniform broadcasts at the start of the step that uses them: during step k the C row of
     // token k (its readout) and the B row of token k+1 (its prelude). Nothing is held across a
@@ -608,16 +633,28 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
 }
 
 // The walk instance for this wave's transition form (wave-uniform).
-template <typename IO, int kMode, bool kGlobalPark, int kVar>
+template <typename IO, int kMode, bool kGlobalPark, int kVar, int kRing = kRingFull>
 __device__ __forceinline__ void walk_as(int form, const ScanArgs& a, const WgCoords& c, Lane& ln, float* lds_park,
                                         const float* lds_c, const float* lds_b, const int32_t* lds_ord, int kbeg,
-                                        int kend, float& dsum) {
+                                        int kend, float& dsum, Ring<ring_depth(kVar)>& rg) {
     if (form == kGeometric)
-        walk<IO, kGeometric, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend, dsum);
+        walk<IO, kGeometric, kMode, kGlobalPark, kVar, kRing>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend,
+                                                              dsum, rg);
     else if (form == kProgression)
-        walk<IO, kProgression, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend, dsum);
+        walk<IO, kProgression, kMode, kGlobalPark, kVar, kRing>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend,
+                                                                dsum, rg);
     else
-        walk<IO, kGeneral, kMode, kGlobalPark, kVar>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend, dsum);
+        walk<IO, kGeneral, kMode, kGlobalPark, kVar, kRing>(a, c, ln, lds_park, lds_c, lds_b, lds_ord, kbeg, kend,
+                                                            dsum, rg);
+}
+
+// Issue the ring loads of a walk that starts at step kbeg (not in a given order).
+template <typename IO, int kMode, bool kGlobalPark, int kVar>
+__device__ __forceinline__ void prime_ring(const ScanArgs& a, const WgCoords& c, Lane& ln, int kbeg, int kend,
+                                           Ring<ring_depth(kVar)>& rg) {
+    float unused = 0.0f;
+    walk<IO, kGeneral, kMode, kGlobalPark, kVar, kRingPrime>(a, c, ln, nullptr, nullptr, nullptr, nullptr, kbeg, kend,
+                                                             unused, rg);
 }
 
 // Copy the chunk's rows into LDS as fp32: regions [C forward, C backward, B forward, B backward]
@@ -735,16 +772,14 @@ __device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCo
 // Main scan: one chunk of one sequence, 64 channels; wave 0 forward, wave 1 backward. The waves
 // meet in the middle of the chunk through the park (LDS, or a global scratch region per
 // workgroup when the chunk is long; see the file header).
-// The state entering chunk `chunk` of direction dir, for the lane's channel dc: the chunk
+// The state entering chunk `chunk` of direction dir, for the lane's channel dc (an = its A row): the chunk
 // aggregates of the chunks before it in scan order folded in the carry combine's order and
 // arithmetic (so bit for bit the combine's result). The loads go kFoldBatch chunks at a time, all
 // issued together, clamped to a chunk whose aggregate exists; only the first cnt enter the fold.
-__device__ __forceinline__ void fold_carry(const ScanArgs& a, int dir, int seq, int chunk, int dc, float (&h)[kN]) {
+__device__ __forceinline__ void fold_carry(const ScanArgs& a, int dir, int seq, int chunk, int dc, const float (&an)[kN],
+                                           float (&h)[kN]) {
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
     const int cnt = dir == 0 ? chunk : a.K - 1 - chunk;  // chunks before this one in scan order
-    float an[kN];
-#pragma unroll
-    for (int n = 0; n < kN; ++n) an[n] = a.A[dir][dc * kN + n];
 #pragma unroll
     for (int n = 0; n < kN; ++n) h[n] = 0.0f;
     for (int j0 = 0; j0 < cnt; j0 += kFoldBatch) {
@@ -777,13 +812,23 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     const float* lds_b = lds + (2 + c.dir) * a.T * kN;
     const int32_t* lds_ord = reinterpret_cast<const int32_t*>(lds + 4 * a.T * kN);
     float* lds_park = lds + 4 * a.T * kN + (kVar == kOrdered ? a.T : 0) + c.sub * a.T * kWave;
-    if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, true);
-    else stage_rows<IO>(a, c, lds, false, true);
+    const int len = c.t1 - c.t0;
+    const int half = len >> 1;
+    const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
     Lane ln;
     ln.init(a, c.dir, c.dc, kConv);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
+    // Loads that need neither the staged rows nor one another are issued before the staging, so
+    // their latency overlaps it: the first walk's rings (in raster order; a given order's tokens
+    // come from the staged copy) and the A row of the transition-form vote.
+    constexpr bool kPrime = kVar != kOrdered;
+    Ring<ring_depth(kVar)> rg;
+    if constexpr (kPrime) prime_ring<IO, kPark, kGlobalPark, kVar>(a, c, ln, 0, n1, rg);
+    const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
+    if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, true);
+    else stage_rows<IO>(a, c, lds, false, true);
     if (kCarry && a.fold) {
-        fold_carry(a, c.dir, c.seq, c.chunk, c.dc, ln.h);
+        fold_carry(a, c.dir, c.seq, c.chunk, c.dc, arow.r, ln.h);
     } else if (kCarry) {
         const float* src = a.carry + ((static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
@@ -792,15 +837,13 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
     }
-    const int form = ln.decay_form(a, c.dir, c.dc);
-    const int len = c.t1 - c.t0;
-    const int half = len >> 1;
-    const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
+    const int form = ln.decay_form(a, arow);
     float unused = 0.0f;
     __syncthreads();  // the rows are staged
-    walk_as<IO, kPark, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, 0, n1, unused);
+    walk_as<IO, kPark, kGlobalPark, kVar, kPrime ? kRingPrimed : kRingFull>(form, a, c, ln, lds_park, lds_c, lds_b,
+                                                                              lds_ord, 0, n1, unused, rg);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
-    walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, n1, len, unused);
+    walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, n1, len, unused, rg);
 }
 
 // Forward-only scan (vimscan_fwd): one chunk of one sequence, every wave a channel block of 64,
@@ -809,11 +852,16 @@ template <typename IO, bool kCarry>
 __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
     extern __shared__ float lds[];  // the chunk's C rows [T][16], then its B rows [T][16]
     const WgCoords c = wg_coords(a, true);
-    stage_rows<IO>(a, c, lds, true, true);
+    const int len = c.t1 - c.t0;
     Lane ln;
     ln.init(a, 0, c.dc, true);
+    // the first walk's rings and the vote's A row go out before the staging (see k_bidir_scan)
+    Ring<ring_depth(kPlain)> rg;
+    prime_ring<IO, kOut, false, kPlain>(a, c, ln, 0, len, rg);
+    const Lane::ARow arow = ln.load_arow(a, 0, c.dc);
+    stage_rows<IO>(a, c, lds, true, true);
     if (kCarry && a.fold) {
-        fold_carry(a, 0, c.seq, c.chunk, c.dc, ln.h);
+        fold_carry(a, 0, c.seq, c.chunk, c.dc, arow.r, ln.h);
     } else if (kCarry) {
         const float* src = a.carry + (static_cast<int64_t>(c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
@@ -822,10 +870,11 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
     }
-    const int form = ln.decay_form(a, 0, c.dc);
+    const int form = ln.decay_form(a, arow);
     float unused = 0.0f;
     __syncthreads();  // the rows are staged
-    walk_as<IO, kOut, false, kPlain>(form, a, c, ln, nullptr, lds, lds + a.T * kN, nullptr, 0, c.t1 - c.t0, unused);
+    walk_as<IO, kOut, false, kPlain, kRingPrimed>(form, a, c, ln, nullptr, lds, lds + a.T * kN, nullptr, 0, len,
+                                                  unused, rg);
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
@@ -835,23 +884,32 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     constexpr bool kConv = kVar == kWithConv;
     extern __shared__ float lds[];  // the chunk's B rows [directions][T][16]; in a given order then the order [T]
     const WgCoords c = wg_coords(a, a.uni != 0);
-    if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, false);
-    else stage_rows<IO>(a, c, lds, a.uni != 0, false);
-    __syncthreads();  // the rows are staged
     // The state after the last chunk in scan order (forward: the last chunk, backward: the first)
-    // is never used, so that chunk's aggregate is not computed (no barrier follows: the wave may
-    // leave).
-    if (c.chunk == (c.dir == 0 ? a.K - 1 : 0)) return;
+    // is never used, so that chunk's aggregate is not computed: its wave only helps stage the rows
+    // and leaves after the barrier.
+    const bool unused_chunk = c.chunk == (c.dir == 0 ? a.K - 1 : 0);
+    const int len = c.t1 - c.t0;
     Lane ln;
     ln.init(a, c.dir, c.dc, false);
     if (kConv) ln.init_conv(a, c.dir, c.dc);
+    // the walk's rings and the vote's A row go out before the staging (see k_bidir_scan)
+    constexpr bool kPrime = kVar != kOrdered;
+    Ring<ring_depth(kVar)> rg;
+    if constexpr (kPrime) {
+        if (!unused_chunk) prime_ring<IO, kAggregate, false, kVar>(a, c, ln, 0, len, rg);
+    }
+    const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
+    if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, false);
+    else stage_rows<IO>(a, c, lds, a.uni != 0, false);
+    __syncthreads();  // the rows are staged
+    if (unused_chunk) return;  // no barrier follows
 #pragma unroll
     for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
-    const int form = ln.decay_form(a, c.dir, c.dc);
-    const int len = c.t1 - c.t0;
+    const int form = ln.decay_form(a, arow);
     float s = 0.0f;
-    walk_as<IO, kAggregate, false, kVar>(form, a, c, ln, nullptr, nullptr, lds + c.dir * a.T * kN,
-                                         reinterpret_cast<const int32_t*>(lds + 2 * a.T * kN), 0, len, s);
+    walk_as<IO, kAggregate, false, kVar, kPrime ? kRingPrimed : kRingFull>(
+        form, a, c, ln, nullptr, nullptr, lds + c.dir * a.T * kN, reinterpret_cast<const int32_t*>(lds + 2 * a.T * kN),
+        0, len, s, rg);
     if (c.valid) {
         const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
         float* dst = a.carry + slot * kN * a.Di;
