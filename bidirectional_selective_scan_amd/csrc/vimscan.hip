@@ -673,7 +673,7 @@ __device__ __forceinline__ const void* region_rows(const ScanArgs& a, int reg, i
 
 template <typename IO>
 __device__ __forceinline__ void stage_rows(const ScanArgs& a, const WgCoords& c, float* lds, bool uni, bool withC) {
-    constexpr int kU = 4;                                      // words per region per thread and pass
+    constexpr int kU = IoTraits<IO>::bytes == 2 ? 7 : 4;       // words per region per thread and pass
     constexpr int kPerWord = 4 / IoTraits<IO>::bytes;          // values per 32-bit word
     using El = typename IoTraits<IO>::elem;
     const int len = c.t1 - c.t0;
