@@ -201,6 +201,7 @@ enum Variant {
 // The state-independent part of one token, computed a token ahead of its state update.
 struct Prelude {
     float delta2, x;     // softplus(dt + bias) * log2(e); x (for the skip term)
+    float u;             // delta2 * x (the walk against the scan order takes only delta2 and u)
     float e[kN];         // transitions exp(delta * A[d, n]) = 2^(delta2 * A[d, n])
     float ub[kN];        // inputs delta2 * x * B[n] (the state is kept scaled by log2(e))
 };
@@ -338,6 +339,41 @@ struct Lane {
         }
         return acc[0] + acc[1];
     }
+
+    // The chunk aggregate (the end state of the chunk's scan from a zero state) walked against
+    // the scan order. A token t adds u_t B_t[n] times the transitions of every token after it in
+    // scan order, prod_{s > t} 2^(delta2_s A[n]) = 2^(S A[n]) with S the sum of delta2 over those
+    // tokens -- the tokens this walk has already passed, so S is the running delta sum itself.
+    // The factored rows give 2^(S A[n]) = E Q^n (E = 2^(S A0), Q = 2^(S dA); geometric: E = Q)
+    // and u enters at the head of that chain: c[n] = u E Q^n, h[n] += c[n] B[n], one product and
+    // one fma per state where the scan-order walk needs three operations (its transition, the
+    // product u B and the fma). Every transition comes straight from the exact suffix sum, not
+    // from a running product.
+    __device__ __forceinline__ Prelude prelude_rev(float xv, float dtv) const {
+        Prelude p;
+        p.delta2 = softplus_log2(dtv, bias2);
+        p.x = xv;
+        p.u = p.delta2 * xv;
+        return p;
+    }
+    template <int kDecay>
+    __device__ __forceinline__ void update_rev(const Prelude& p, const float (&Bv)[kN], const Rates<kDecay>& r,
+                                               float S) {
+        if constexpr (kDecay == kGeneral) {
+#pragma unroll
+            for (int n = 0; n < kN; ++n) h[n] = fmaf(p.u * fast_exp2(S * r.an[n]), Bv[n], h[n]);
+        } else {
+            const float Q = fast_exp2(S * r.da);
+            float cn;
+            if constexpr (kDecay == kGeometric) cn = p.u * Q;
+            else cn = p.u * fast_exp2(S * r.a0);
+#pragma unroll
+            for (int n = 0; n < kN; ++n) {
+                h[n] = fmaf(cn, Bv[n], h[n]);
+                if (n + 1 < kN) cn *= Q;
+            }
+        }
+    }
 };
 
 struct WgCoords {
@@ -373,7 +409,8 @@ enum WalkMode {
     kPark = 0,      // first half of a chunk: park this direction's output (LDS or global scratch)
     kFinish = 1,    // second half: add the other direction's parked output, gate, store y
     kAggregate = 2, // chunk pass 1: no readout, accumulate sum(delta)
-    kOut = 3        // forward only: gate and store every token (no park, no other direction)
+    kOut = 3,       // forward only: gate and store every token (no park, no other direction)
+    kAggRev = 4     // chunk pass 1 walked against the scan order (see Lane::update_rev)
 };
 
 // The register rings of a walk (see walk): raw x and dt of the steps ahead, z and the parked
@@ -416,7 +453,9 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     static_assert(!(kOrd && kRing != kRingFull), "an ordered walk's tokens come from LDS: it fills its own rings");
     constexpr int P = ring_depth(kVar);  // ring depth (tokens prefetched ahead); the window takes the registers of one slot
     constexpr uint32_t e = IoTraits<IO>::bytes;
-    constexpr bool kReadout = kMode != kAggregate;
+    constexpr bool kRev = kMode == kAggRev;
+    constexpr bool kReadout = kMode != kAggregate && !kRev;
+    static_assert(!(kRev && kConv), "the convolution's window follows the scan order");
     using E = typename IoTraits<IO>::elem;
     if (kbeg >= kend) return;
     const int len = c.t1 - c.t0;
@@ -442,8 +481,9 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
     // Local token index of walk step k: k forward, len-1-k backward, as base + sign*k with
     // wave-uniform base and sign. Both directions run this same code: a separate instance per
     // direction puts two different hot loops on every CU and measured much slower.
-    const int sgn = 1 - 2 * c.dir;
-    const int tbase = c.dir * (len - 1);
+    const int rdir = kRev ? 1 - c.dir : c.dir;  // the order of the walk
+    const int sgn = 1 - 2 * rdir;
+    const int tbase = rdir * (len - 1);
     auto lt = [&](int k) { return tbase + sgn * k; };
     // Token row (from rbase) of walk step min(k, last): the step itself, or in a given order the
     // token the order lists for it, read from the chunk's copy of the order in LDS (a broadcast
@@ -533,8 +573,13 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             v[4 * q + 3] = f.w;
         }
     };
-    lds_row(lds_b, kbeg, Bn);
-    Prelude cur = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
+    Prelude cur;
+    if constexpr (kRev) {
+        cur = ln.prelude_rev(widen(IO{}, xr[0]), widen(IO{}, dr[0]));
+    } else {
+        lds_row(lds_b, kbeg, Bn);
+        cur = ln.template prelude<kDecay>(input(widen(IO{}, xr[0])), widen(IO{}, dr[0]), Bn, rates);
+    }
     {
         uint32_t so;
         if constexpr (kOrd) {
@@ -554,7 +599,7 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
         const int jn = (j + 1) % P;
         const int tl = lt(kk);
         if (kReadout) lds_row(lds_c, kk, Cv);  // this token's C row
-        lds_row(lds_b, kk + 1, Bn);  // next token's B row, for its prelude below
+        lds_row(lds_b, kRev ? kk : kk + 1, Bn);  // next token's B row for its prelude (kRev: this token's)
         // Consume the ring slots before refilling them: the empty asm takes the widened values
         // and orders every load after it, so a refill can reuse its slot's register and the loop
         // needs no register copies (a copy would wait for the load just issued).
@@ -590,9 +635,17 @@ __device__ __forceinline__ void walk(const ScanArgs& a, const WgCoords& c, Lane&
             zr[j] = ld_raw(IO{}, rz, vo, so);
             if (kMode == kFinish && kGlobalPark) pr[j] = __builtin_amdgcn_raw_buffer_load_b32(rp, vp, poff(kk + P), 0);
         }
-        const Prelude nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);  // next token's prelude
+        Prelude nxt;  // next token's prelude
+        if constexpr (kRev) nxt = ln.prelude_rev(xn, dn);
+        else nxt = ln.template prelude<kDecay>(input(xn), dn, Bn, rates);
         if (kMode == kAggregate) dsum += cur.delta2;
-        float yv = ln.template update<kReadout>(cur, Cv);
+        float yv = 0.0f;
+        if constexpr (kRev) {
+            ln.template update_rev<kDecay>(cur, Bn, rates, dsum);  // dsum: the suffix sum S so far
+            dsum += cur.delta2;
+        } else {
+            yv = ln.template update<kReadout>(cur, Cv);
+        }
         if (kConv && kReadout) yv = fmaf(ln.Dd, cur.x, yv);  // own skip term on own input u
         if (kMode == kPark) {
             if (kGlobalPark)
@@ -878,10 +931,12 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
 }
 
 // Pass 1 of the chunked scan: per chunk and direction, the end state of the chunk's local scan
-// from a zero state, and the sum of delta over the chunk.
+// from a zero state, and the sum of delta over the chunk. The walk goes against the scan order
+// (Lane::update_rev), except with the convolution, whose input window follows the scan order.
 template <typename IO, int kVar>
 __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     constexpr bool kConv = kVar == kWithConv;
+    constexpr int kAggMode = kConv ? kAggregate : kAggRev;
     extern __shared__ float lds[];  // the chunk's B rows [directions][T][16]; in a given order then the order [T]
     const WgCoords c = wg_coords(a, a.uni != 0);
     // The state after the last chunk in scan order (forward: the last chunk, backward: the first)
@@ -896,7 +951,7 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     constexpr bool kPrime = kVar != kOrdered;
     Ring<ring_depth(kVar)> rg;
     if constexpr (kPrime) {
-        if (!unused_chunk) prime_ring<IO, kAggregate, false, kVar>(a, c, ln, 0, len, rg);
+        if (!unused_chunk) prime_ring<IO, kAggMode, false, kVar>(a, c, ln, 0, len, rg);
     }
     const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
     if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, false);
@@ -907,7 +962,7 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
     const int form = ln.decay_form(a, arow);
     float s = 0.0f;
-    walk_as<IO, kAggregate, false, kVar, kPrime ? kRingPrimed : kRingFull>(
+    walk_as<IO, kAggMode, false, kVar, kPrime ? kRingPrimed : kRingFull>(
         form, a, c, ln, nullptr, nullptr, lds + c.dir * a.T * kN, reinterpret_cast<const int32_t*>(lds + 2 * a.T * kN),
         0, len, s, rg);
     if (c.valid) {
