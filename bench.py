@@ -199,6 +199,89 @@ def configs_leg(graph_wall, dev, steps, headline=None, with_cpu=True):
     return res
 
 
+# Shapes of the forced-chunk sweep (--chunk-sweep): the five workloads and five more of the same
+# family, bidirectional, then three forward only (batch, tokens, d_inner, io dtype, seg_len,
+# forward only).
+SWEEP_SHAPES = [
+    (2, 65, 32, "f32", 0, False), (64, 197, 384, "f32", 0, False), (128, 197, 768, "bf16", 0, False),
+    (8, 1025, 768, "bf16", 0, False), (1, 13056, 1536, "bf16", 51, False), (1, 1025, 768, "bf16", 0, False),
+    (2, 4097, 768, "bf16", 0, False), (16, 197, 768, "bf16", 0, False), (8, 577, 768, "bf16", 0, False),
+    (32, 257, 192, "f32", 0, False),
+    (128, 197, 768, "bf16", 0, True), (64, 197, 384, "f32", 0, True), (8, 1025, 768, "bf16", 0, True),
+]
+SWEEP_CHUNK_COUNTS = (1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 20, 24, 28, 32, 40, 48, 64, 80, 96, 128)
+
+
+def chunk_sweep(dev, steps, warmup, settle_s):
+    """Every shape of SWEEP_SHAPES with the plan's own chunking and with forced chunk lengths: the
+    even split ceil(L / K) into K chunks for each K of SWEEP_CHUNK_COUNTS that gives 8 to 256
+    tokens per chunk. HIP graph replays of the whole call on rotating input copies, microseconds
+    per call. Prints one JSON line per shape and returns them."""
+    import torch
+    from bidirectional_selective_scan_amd import binding
+    from bidirectional_selective_scan_amd.inputs import device_inputs
+    io_names = ("x", "dt", "z", "B_f", "C_f", "B_b", "C_b")
+    par_names = ("A_f", "A_b", "D_f", "D_b", "dt_bias_f", "dt_bias_b")
+    out = []
+    for B, L, Di, io, seg, fwd in SWEEP_SHAPES:
+        Lp = seg or L
+        inp = device_inputs(B, L, Di, 16, io, seed=0, device=str(dev))
+        nbytes = sum(int(inp[k].numel() * inp[k].element_size()) for k in io_names) + B * L * Di * (2 if io == "bf16" else 4)
+        n = min(64, max(2, -(-2 * CACHE_BYTES // nbytes) + 1))
+        copies = [[inp[k].clone() for k in io_names] for _ in range(n)]
+        outs = [torch.empty_like(inp["x"]) for _ in range(n)]
+        params = [inp[k] for k in par_names]
+        plan = binding.launch_info(B, L, Di, 16, seg, io, forward_only=fwd)
+
+        def prep(i, T, ws):
+            if fwd:
+                return binding.prepare_fwd(*copies[i][:5], params[0], params[2], params[4], seg_len=seg, out=outs[i],
+                                           chunk_len=T, workspace=ws, stream=torch.cuda.current_stream().cuda_stream)
+            return binding.PreparedCall(*copies[i], *params, seg_len=seg, out=outs[i], workspace=ws, chunk_len=T,
+                                        stream=torch.cuda.current_stream().cuda_stream)
+        cands = [0] + sorted({-(-Lp // K) for K in SWEEP_CHUNK_COUNTS if 8 <= -(-Lp // K) <= 256})
+        times = {}
+        for T in cands:
+            wsb = binding.workspace_bytes(B, L, Di, 16, seg, io, chunk_len=T, forward_only=fwd)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+            calls = [prep(i, T, ws) for i in range(n)]
+            for c in calls:
+                c()
+            torch.cuda.synchronize(dev)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in [prep(i, T, ws) for i in range(n)]:
+                    c()
+            t_end = time.perf_counter() + settle_s
+            while True:   # clock ramp, then warm-up replays
+                g.replay()
+                torch.cuda.synchronize(dev)
+                if time.perf_counter() >= t_end:
+                    break
+            reps = max(1, warmup // n)
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize(dev)
+            reps = max(1, -(-steps // n))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize(dev)
+            times[T] = (time.perf_counter() - t0) / (reps * n) * 1e6
+            del g, calls, ws
+        forced = {T: v for T, v in times.items() if T}
+        best_T = min(forced, key=forced.get)
+        rec = {"shape": {"batch": B, "seqlen": L, "d_inner": Di, "io": io, "seg_len": seg, "forward_only": fwd},
+               "plan": {"chunk_len": plan["chunk_len"], "chunks": plan["chunks"], "kernels": plan["kernels"]},
+               "plan_us": round(times[0], 2), "best_chunk_len": best_T, "best_us": round(forced[best_T], 2),
+               "plan_over_best": round(times[0] / forced[best_T], 4),
+               "us_by_chunk_len": {str(T): round(v, 2) for T, v in forced.items()}}
+        print(json.dumps(rec), flush=True)
+        out.append(rec)
+        del copies, outs, inp
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +312,8 @@ def main(argv=None):
                     help="time the headline steps as eager library calls instead of HIP graph replays")
     ap.add_argument("--only-ncssd", action="store_true",
                     help="measure only the NC-SSD global-state form (for its counter runs)")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="only time every sweep shape with the plan's chunking and with forced chunk lengths")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-mebibyte buffer 5 times (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -246,6 +331,12 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return 0
+    if args.chunk_sweep:
+        recs = chunk_sweep(torch.device("cuda:0"), args.steps, args.warmup, args.settle)
+        worst = max(r["plan_over_best"] for r in recs)
+        print(json.dumps({"chunk_sweep_shapes": len(recs), "worst_plan_over_best": worst,
+                          "within_3pct": sum(r["plan_over_best"] <= 1.03 for r in recs)}), flush=True)
         return 0
     from bidirectional_selective_scan_amd import binding
     from bidirectional_selective_scan_amd.configs import HEADLINE, WORKLOADS

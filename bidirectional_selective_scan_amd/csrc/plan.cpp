@@ -12,11 +12,6 @@ namespace {
 
 
 
-// Forward only: a single pass needs at least this many waves (channel blocks x sequences), and a
-// chunked plan aims at this many.
-constexpr int64_t kUniSinglePass = 1024;
-constexpr int64_t kUniTarget = 3072;
-
 // An MI355X: 256 compute units with 160 KB of LDS each.
 constexpr int64_t kCus = 256;
 constexpr int64_t kLdsPerCu = 160 * 1024;
@@ -36,20 +31,75 @@ int64_t resident_wgs(const ScanPlan* p, int io_dtype, int64_t T) {
     return r;
 }
 
-// Modelled time of a chunked pass with chunks of T tokens. The busiest CU runs ceil(wgs / 256)
-// workgroups, in rounds of at most resident_wgs; a round of a workgroups on a CU costs a / e(a)
-// per token, e(a) being the issue efficiency of the VALU-bound token loop with a waves per SIMD
-// (about 0.5 for a lone wave, 0.9 and more from two on, as measured on this kernel), and each
-// chunk adds about 8 tokens' worth of fixed work (staging, carries).
-double chunk_cost(const ScanPlan* p, int io_dtype, int64_t T) {
-    static const double eff[4] = {0.5, 0.9, 0.92, 0.95};
-    const int64_t K = (p->Lp + T - 1) / T;
-    const int64_t wgs = p->nseq * K * ((p->ncb + p->subs - 1) / p->subs);
-    const int64_t per_cu = (wgs + kCus - 1) / kCus;
+// Issue efficiency of the VALU-bound token loop with a waves per SIMD (a lone wave leaves about
+// half the issue slots empty), and the cost in token steps of a round of a workgroups on a CU.
+double round_cost(int64_t a) {
+    static const double eff[5] = {0.505, 0.80, 0.95, 0.97, 0.98};
+    return static_cast<double>(a) / eff[a < 5 ? a - 1 : 4];
+}
+
+// Cost of per_cu workgroups on the busiest CU, r at a time.
+double rounds(int64_t per_cu, int64_t r) {
+    const int64_t n = per_cu / r, rest = per_cu % r;
+    return static_cast<double>(n) * round_cost(r) + (rest ? round_cost(rest) : 0.0);
+}
+
+// Chunk count of the forward-only scan: a single pass from 1024 waves (channel blocks x
+// sequences) on, else first enough chunks for 3072 waves (at least 32 tokens per chunk) and,
+// when that leaves only a few rounds of workgroups per CU, the count of least modelled scan time
+// up to twice as many chunks and down to 16 tokens per chunk: T + 8 token steps per workgroup in
+// rounds of resident_wgs, at an issue efficiency of 0.5, 0.9, 0.92, 0.95 with 1, 2, 3, 4 waves
+// per SIMD. (Measured on the forward-only shapes of the forced-chunk sweep, this plan is within
+// 4% of the best chunk count where the bidirectional model below misses by up to 13%.)
+int64_t uni_chunks(const ScanPlan* p, int io_dtype) {
+    const int64_t lanes = p->nseq * p->ncb;
+    const int64_t kmin = (p->Lp + kMaxChunk - 1) / kMaxChunk;
+    if (p->Lp <= kMaxChunk && lanes >= 1024) return 1;
+    const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;
+    int64_t K = std::min(std::max((3072 + lanes - 1) / lanes, kmin), std::max(kmin, (p->Lp + 31) / 32));
+    auto cost = [&](int64_t k) {
+        static const double eff[4] = {0.5, 0.9, 0.92, 0.95};
+        const int64_t T = (p->Lp + k - 1) / k;
+        const int64_t per_cu = (p->nseq * k * wpc + kCus - 1) / kCus;
+        const int64_t r = resident_wgs(p, io_dtype, T);
+        auto rc = [&](int64_t a) { return static_cast<double>(a) / eff[a < 4 ? a - 1 : 3]; };
+        return static_cast<double>(T + 8) * (static_cast<double>(per_cu / r) * rc(r) + (per_cu % r ? rc(per_cu % r) : 0.0));
+    };
+    if (p->nseq * K * wpc <= 4 * kCus * resident_wgs(p, io_dtype, (p->Lp + K - 1) / K)) {
+        const int64_t khi = std::max(kmin, std::min((p->Lp + 15) / 16, 2 * K));
+        double best = -1.0;
+        for (int64_t k = kmin; k <= khi; ++k) {
+            const double c = cost(k);
+            if (best < 0.0 || c < best) best = c, K = k;
+        }
+    }
+    return K;
+}
+
+// Modelled time of a whole call with chunks of about Lp / K tokens, in units of one token step of
+// a round of workgroups (about 0.15 us on this chip). Terms, fitted to a sweep of forced chunk
+// counts over ten shapes of the Vim family (see the forced-chunk sweep of bench.py):
+//  * the scan kernel: T + 7.7 token steps per workgroup (the staging, the rings and the carry
+//    load are worth 7.7 tokens), in rounds of resident_wgs;
+//  * with 2..kFoldMaxChunks chunks, the fold of the earlier aggregates in the scan kernel: 5.9 per
+//    batch of 4 aggregates per round (a memory round trip each);
+//  * with chunks, the aggregate pass: 0.31 of a scan token step per token (no readout; walked
+//    against the scan order) plus 37 for its staging and stores, at up to 5 workgroups per CU;
+//  * past kFoldMaxChunks, the combine kernel: 2.9 + 15.3 per 16 chunks (each a batch of loads);
+//  * 29 per kernel after the first (launch and drain).
+double plan_cost(const ScanPlan* p, int io_dtype, int64_t K) {
+    const int64_t T = (p->Lp + K - 1) / K;
+    const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;
+    const int64_t per_cu = (p->nseq * K * wpc + kCus - 1) / kCus;
     const int64_t r = resident_wgs(p, io_dtype, T);
-    auto round_cost = [&](int64_t a) { return a / eff[a < 4 ? a - 1 : 3]; };
-    const int64_t rounds = per_cu / r, rest = per_cu % r;
-    return static_cast<double>(T + 8) * (rounds * round_cost(r) + (rest ? round_cost(rest) : 0.0));
+    const int64_t nr = (per_cu + r - 1) / r;
+    double c = static_cast<double>(T + 7.7) * rounds(per_cu, r);
+    if (K > 1) {
+        c += 0.31 * static_cast<double>(T + 37) * rounds(per_cu, std::min<int64_t>(5, kLdsPerCu / (T * kN * 8 + 1)));
+        if (K <= kFoldMaxChunks) c += 5.9 * static_cast<double>((K - 1 + 3) / 4 * nr) + 29.0;
+        else c += 2.9 + 15.3 * static_cast<double>((K + 15) / 16) + 2 * 29.0;
+    }
+    return c;
 }
 
 const char* const kStatusText[] = {
@@ -112,45 +162,33 @@ int make_scan_plan(const vimscan_launch* l, int64_t seg_len, ScanPlan* p) {
     p->ncb = (l->d_inner + kWave - 1) / kWave;
     p->uni = (l->flags & VIMSCAN_FLAG_FORWARD_ONLY) != 0;
     p->swap = (l->flags & VIMSCAN_FLAG_AUX_SWAP) != 0;
-    // Units of parallel work of a single pass: wave pairs (forward + backward), or single waves
-    // forward only; a chunked plan aims at 1536 of them (3 waves per SIMD bidirectional).
-    const int64_t lanes = p->nseq * p->ncb;
-    const int64_t target = p->uni ? kUniTarget : 1536;
     // Four waves per workgroup (two channel blocks x two directions, or four channel blocks
     // forward only) when there are enough channel blocks: the hardware spreads a 4-wave
     // workgroup over the CU's four SIMDs, where 2-wave workgroups can leave some SIMDs with twice
     // the waves of others.
     if (p->uni) p->subs = p->ncb >= 4 ? 4 : p->ncb;
     else p->subs = p->ncb >= 2 ? 2 : 1;
-    const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;  // workgroups per sequence and chunk
-    // A bidirectional single pass with at most one workgroup per CU gives each SIMD a lone wave
-    // (Vim-Ti: 192 workgroups on 256 CUs): from 64 tokens on, chunking to the wave-pair target
-    // pays for the aggregate pass (Vim-Ti: 4 chunks of 50, 72.9 -> 66.0 us per call).
-    const bool single = (p->Lp <= kMaxChunk && lanes >= (p->uni ? kUniSinglePass : 256)) || p->Lp <= 32;
-    const bool sparse = single && !p->uni && p->Lp >= 64 && p->nseq * wpc <= kCus;
+    // Bidirectional: the chunk count of least modelled time (plan_cost), from the fewest chunks of
+    // at most kMaxChunk tokens (a single pass when the sequence fits one) to chunks of 8 tokens.
+    // Forward only: uni_chunks. Sequences of up to 32 tokens are never chunked.
     int64_t T;
     if (l->chunk_len > 0) {
         T = l->chunk_len;
-    } else if (single && !sparse) {
-        T = p->Lp;  // single pass: enough workgroups, or too short to be worth chunking
+    } else if (p->Lp <= 32) {
+        T = p->Lp;
+    } else if (p->uni) {
+        const int64_t K = uni_chunks(p, l->io_dtype);
+        T = (p->Lp + K - 1) / K;
     } else {
-        // Chunk for parallelism: first enough chunks for `target` waves, with at least 32 tokens
-        // per chunk.
-        int64_t K = (target + lanes - 1) / lanes;
         const int64_t kmin = (p->Lp + kMaxChunk - 1) / kMaxChunk;
-        const int64_t kmax = (p->Lp + 31) / 32;
-        if (K < kmin) K = kmin;
-        if (K > kmax) K = kmax;
-        // When that leaves only a few rounds of workgroups per CU, a round that is partly empty
-        // costs as much as a full one: take instead the chunk count of least modelled time, up
-        // to twice as many chunks and down to 16 tokens per chunk.
-        if (!sparse && p->nseq * K * wpc <= 4 * kCus * resident_wgs(p, l->io_dtype, (p->Lp + K - 1) / K)) {
-            const int64_t khi = std::min((p->Lp + 15) / 16, 2 * K);
-            double best = -1.0;
-            for (int64_t k = kmin; k <= khi; ++k) {
-                const double c = chunk_cost(p, l->io_dtype, (p->Lp + k - 1) / k);
-                if (best < 0.0 || c < best) best = c, K = k;
-            }
+        const int64_t kmax = std::max(kmin, (p->Lp + 7) / 8);
+        int64_t K = kmin;
+        double best = -1.0;
+        for (int64_t k = kmin; k <= kmax; ++k) {
+            const int64_t t = (p->Lp + k - 1) / k;
+            if ((p->Lp + t - 1) / t != k) continue;  // k chunks of t tokens: fewer chunks cover the sequence
+            const double c = plan_cost(p, l->io_dtype, k);
+            if (best < 0.0 || c < best) best = c, K = k;
         }
         T = (p->Lp + K - 1) / K;
     }

@@ -20,7 +20,7 @@ constexpr int kMaxChunk = 256;      // tokens per chunk
 constexpr int kMaxTaps = 4;         // taps of the directional convolution
 // Plans of up to kFoldMaxChunks chunks run without the carry combine kernel: each scan workgroup
 // folds the chunk aggregates before its chunk itself.
-constexpr int kFoldMaxChunks = 32;
+constexpr int kFoldMaxChunks = 16;
 // A park larger than this goes to global scratch: in LDS it would cap a CU at fewer than 8
 // workgroups, and the VALU needs several waves per SIMD to issue at full rate.
 constexpr int64_t kLdsParkMaxBytes = 20 * 1024;

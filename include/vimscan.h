@@ -141,8 +141,8 @@ typedef struct vimscan_plan {
     int64_t chunks;         /* chunks per sequence; 1 = single pass (no chunk carries) */
     int64_t workgroups;     /* workgroups of the main scan kernel */
     int32_t kernels;        /* kernels launched per call: the main scan, plus 1 when chunked
-                               (chunk aggregates), plus 1 more beyond 32 chunks per sequence
-                               (carry combine; up to 32 the scan workgroups fold the aggregates
+                               (chunk aggregates), plus 1 more beyond 16 chunks per sequence
+                               (carry combine; up to 16 the scan workgroups fold the aggregates
                                themselves), plus 1 with VIMSCAN_FLAG_AUX_SWAP */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */

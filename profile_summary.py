@@ -19,6 +19,11 @@
       wave, the fraction of time the VALU was busy (SQ_ACTIVE_INST_VALU is in quad-cycles per SIMD,
       so busy = sum / CUs / GRBM_GUI_ACTIVE of one XCD), the shader clock implied by
       GRBM_GUI_ACTIVE over the dispatch time, and the share of waves' time spent waiting.
+
+  python profile_summary.py sweep --jsonl <bench.py --chunk-sweep output> --cmd "<command>"
+      --out profiles/<name>.txt
+      the forced-chunk sweep as a table: per shape the plan's chunking and time, the best forced
+      chunk length and time, their ratio, and every forced length's time.
 """
 from __future__ import annotations
 
@@ -81,7 +86,38 @@ def main():
     v.add_argument("--skip", type=int, default=0, help="ignore the first N dispatches of the kernel")
     v.add_argument("--take", type=int, default=0, help="then use N dispatches (0: all the rest)")
     v.add_argument("--xcds", type=int, default=8)
+    w = sub.add_parser("sweep")
+    for k in ("jsonl", "cmd", "out"):
+        w.add_argument("--" + k, required=True)
     a = ap.parse_args()
+
+    if a.what == "sweep":
+        recs = [json.loads(x) for x in open(a.jsonl) if x.strip().startswith("{")]
+        shapes = [r for r in recs if "shape" in r]
+        lines = [f"command: {a.cmd}", "",
+                 "HIP graph replays of the whole call (all kernels of the plan), rotating input copies; us per call.",
+                 "plan = the library's own chunking (chunk_len 0); forced = each even split into K chunks.", "",
+                 f"{'shape (batch, tokens, d_inner, io, seg_len, fwd)':50s} {'plan T x K':>11s} {'kern':>4s} "
+                 f"{'plan_us':>8s} {'best T':>6s} {'best_us':>8s} {'plan/best':>9s}"]
+        for r in shapes:
+            sh = r["shape"]
+            name = (f"({sh['batch']}, {sh['seqlen']}, {sh['d_inner']}, {sh['io']}, {sh['seg_len']}, "
+                    f"{'fwd' if sh.get('forward_only') else 'bidir'})")
+            pl = r["plan"]
+            lines.append(f"{name:50s} {str(pl['chunk_len']) + ' x ' + str(pl['chunks']):>11s} {pl['kernels']:4d} "
+                         f"{r['plan_us']:8.2f} {r['best_chunk_len']:6d} {r['best_us']:8.2f} {r['plan_over_best']:9.4f}")
+        n3 = sum(r["plan_over_best"] <= 1.03 for r in shapes)
+        lines += ["", f"plan within 3% of the best forced chunk length: {n3} of {len(shapes)} shapes; "
+                      f"worst plan/best {max(r['plan_over_best'] for r in shapes):.4f}", "",
+                  "every forced chunk length (T: us per call):"]
+        for r in shapes:
+            sh = r["shape"]
+            lines.append(f"  ({sh['batch']}, {sh['seqlen']}, {sh['d_inner']}, {sh['io']}, {sh['seg_len']}, "
+                         f"{'fwd' if sh.get('forward_only') else 'bidir'}): " +
+                         " ".join(f"{t}:{v}" for t, v in r["us_by_chunk_len"].items()))
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
 
     if a.what == "valu":
         per = collections.defaultdict(lambda: collections.defaultdict(float))

@@ -34,7 +34,7 @@ from bidirectional_selective_scan_amd.configs import WORKLOADS
 N = 16
 WAVE = 64
 LDS_PER_CU = 160 * 1024
-FOLD_MAX = 32
+FOLD_MAX = 16
 
 
 def xcd_remap(i, n):
@@ -328,7 +328,7 @@ def test_random_sweep_and_fold_boundaries(variant):
         Di = int(rng.integers(1, 200))
         chunk = int(rng.integers(1, min(seg or L, 256) + 1)) if rng.random() < 0.4 else 0
         replay_scan(B, L, Di, ("f32", "bf16")[int(rng.integers(2))], seg, chunk, variant, int(rng.integers(1, 5)))
-    for k in (2, 3, 4, 5, 6, 9, 16, 32, 33):            # 7-token chunks: fold batches and the combine
+    for k in (2, 3, 4, 5, 6, 9, 13, 16, 17, 32, 33):    # 7-token chunks: fold batches and the combine
         replay_scan(2, 7 * k - 3, 96, "bf16", 0, 7, variant)
 
 
