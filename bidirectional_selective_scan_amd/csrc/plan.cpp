@@ -34,7 +34,7 @@ int64_t resident_wgs(const ScanPlan* p, int io_dtype, int64_t T) {
 // Issue efficiency of the VALU-bound token loop with a waves per SIMD (a lone wave leaves about
 // half the issue slots empty), and the cost in token steps of a round of a workgroups on a CU.
 double round_cost(int64_t a) {
-    static const double eff[5] = {0.505, 0.80, 0.95, 0.97, 0.98};
+    static const double eff[5] = {0.531, 0.841, 0.95, 0.97, 0.98};
     return static_cast<double>(a) / eff[a < 5 ? a - 1 : 4];
 }
 
@@ -77,27 +77,31 @@ int64_t uni_chunks(const ScanPlan* p, int io_dtype) {
 }
 
 // Modelled time of a whole call with chunks of about Lp / K tokens, in units of one token step of
-// a round of workgroups (about 0.15 us on this chip). Terms, fitted to a sweep of forced chunk
-// counts over ten shapes of the Vim family (see the forced-chunk sweep of bench.py):
-//  * the scan kernel: T + 7.7 token steps per workgroup (the staging, the rings and the carry
-//    load are worth 7.7 tokens), in rounds of resident_wgs;
-//  * with 2..kFoldMaxChunks chunks, the fold of the earlier aggregates in the scan kernel: 5.9 per
-//    batch of 4 aggregates per round (a memory round trip each);
-//  * with chunks, the aggregate pass: 0.31 of a scan token step per token (no readout; walked
-//    against the scan order) plus 37 for its staging and stores, at up to 5 workgroups per CU;
-//  * past kFoldMaxChunks, the combine kernel: 2.9 + 15.3 per 16 chunks (each a batch of loads);
-//  * 29 per kernel after the first (launch and drain).
+// a round of workgroups (about 0.17 us on this chip). Terms, fitted to a sweep of forced chunk
+// counts over ten bidirectional shapes of the Vim family (the forced-chunk sweep of bench.py;
+// points within 1.6x of each shape's best):
+//  * the scan: T token steps per workgroup, in rounds of resident_wgs;
+//  * with 2..kFoldMaxChunks chunks, the one-pass kernel's own aggregate walk (no readout, walked
+//    against the scan order) at 0.296 of a scan step per token plus 62.9 for its staging, stores
+//    and hand-over, in the same rounds, and 2.66 per chunk of the sequence per round for the wait
+//    on the other chunks and the fold of their aggregates;
+//  * past kFoldMaxChunks, the separate aggregate pass: 0.139 of a scan step per token plus 109.6,
+//    at up to 5 workgroups per CU; the combine kernel: 3.86 + 14.0 per 16 chunks; 32.2 for each of
+//    the two kernels after the first (launch and drain).
 double plan_cost(const ScanPlan* p, int io_dtype, int64_t K) {
     const int64_t T = (p->Lp + K - 1) / K;
     const int64_t wpc = (p->ncb + p->subs - 1) / p->subs;
     const int64_t per_cu = (p->nseq * K * wpc + kCus - 1) / kCus;
     const int64_t r = resident_wgs(p, io_dtype, T);
     const int64_t nr = (per_cu + r - 1) / r;
-    double c = static_cast<double>(T + 7.7) * rounds(per_cu, r);
-    if (K > 1) {
-        c += 0.31 * static_cast<double>(T + 37) * rounds(per_cu, std::min<int64_t>(5, kLdsPerCu / (T * kN * 8 + 1)));
-        if (K <= kFoldMaxChunks) c += 5.9 * static_cast<double>((K - 1 + 3) / 4 * nr) + 29.0;
-        else c += 2.9 + 15.3 * static_cast<double>((K + 15) / 16) + 2 * 29.0;
+    const double rs = rounds(per_cu, r);
+    const double t = static_cast<double>(T);
+    double c = t * rs;
+    if (K > 1 && K <= kFoldMaxChunks) {
+        c += 0.296 * (t + 62.9) * rs + 2.66 * static_cast<double>(K * nr);
+    } else if (K > kFoldMaxChunks) {
+        c += 0.139 * (t + 109.6) * rounds(per_cu, std::min<int64_t>(5, kLdsPerCu / (T * kN * 8 + 1)));
+        c += 3.86 + 14.0 * static_cast<double>((K + 15) / 16) + 2 * 32.2;
     }
     return c;
 }
@@ -200,16 +204,21 @@ int make_scan_plan(const vimscan_launch* l, int64_t seg_len, ScanPlan* p) {
     // With few chunks every scan workgroup folds the aggregates before its chunk itself: no
     // combine kernel, and the carries are written once and read, not rewritten.
     p->fold = p->K > 1 && p->K <= kFoldMaxChunks;
-    p->kernels = (p->K > 1 ? (p->fold ? 2 : 3) : 1) + (p->swap ? 1 : 0);
+    // Bidirectional, those plans run as one kernel: every workgroup computes its own chunk's
+    // aggregates, publishes them and folds those of the chunks before it (k_bidir_chain).
+    p->chain = p->fold && !p->uni;
+    p->kernels = (p->K > 1 ? (p->chain ? 1 : p->fold ? 2 : 3) : 1) + (p->swap ? 1 : 0);
     p->park_global = !p->uni && p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
     const size_t f = sizeof(float);
     const size_t ndir = p->uni ? 1 : 2;
     const size_t carry = p->K > 1 ? static_cast<size_t>(ndir * p->nseq * p->K) * kN * l->d_inner * f : 0;
     const size_t dsum = p->K > 1 ? static_cast<size_t>(ndir * p->nseq * p->K) * l->d_inner * f : 0;
     const size_t park = p->park_global ? static_cast<size_t>(p->wgs) * p->subs * p->T * kWave * f : 0;
+    const size_t tags = p->chain ? static_cast<size_t>(ndir * p->nseq * p->K * p->ncb) * sizeof(uint64_t) : 0;
     p->off_dsum = round_up(carry, 256);
     p->off_park = round_up(p->off_dsum + dsum, 256);
-    p->ws = (carry + dsum + park) > 0 ? p->off_park + park : 0;
+    p->off_tags = round_up(p->off_park + park, 256);
+    p->ws = (carry + dsum + park + tags) > 0 ? p->off_tags + tags : 0;
     return VIMSCAN_OK;
 }
 

@@ -40,8 +40,9 @@ struct ScanPlan {
     int64_t nseq, Lp, T, K, ncb, subs, wgs;
     int kernels;
     bool park_global, uni, swap, fold;
+    bool chain;                                // bidirectional with 2..kFoldMaxChunks chunks: one kernel
     size_t ws;                                 // total scratch bytes
-    size_t off_dsum, off_park;                // byte offsets of the regions after the carries
+    size_t off_dsum, off_park, off_tags;      // byte offsets of the regions after the carries
 };
 
 // Shape, dtype, seg_len, chunk_len and flag checks of a scan launch.

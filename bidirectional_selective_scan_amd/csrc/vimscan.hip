@@ -183,6 +183,7 @@ struct ScanArgs {
     int uni;             // 1: forward only (vimscan_fwd): every wave of a workgroup is a channel block
     const int32_t* order;  // kOrdered: [nseq][Lp] the token each scan step visits (vimscan_bidir_order_fwd)
     int fold;              // chunked: 1 when each scan workgroup folds the chunk aggregates itself
+    uint64_t* tags;        // one-pass chunked (k_bidir_chain): [dir][seq][chunk][ncb] publication tags; else null
 };
 
 // The directional convolution carries kMaxTaps taps (a layer with fewer taps is run with the
@@ -381,15 +382,27 @@ struct WgCoords {
     bool valid;
 };
 
+// One-pass chunked scan (kChain): the chunks of one (sequence, channel-block group) take
+// consecutive workgroup ids, chunk fastest, in hardware order (no XCD remap): a workgroup waits only
+// for the other chunks of its group, which the in-order dispatch has started or starts next.
+template <bool kChain = false>
 __device__ __forceinline__ WgCoords wg_coords(const ScanArgs& a, bool uni) {
     WgCoords c;
-    const int lid = xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int lid = kChain ? static_cast<int>(blockIdx.x) : xcd_remap(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int ncbw = (a.ncb + a.subs - 1) / a.subs;  // channel-block groups per sequence
     c.lid = lid;
-    const int cbw = lid % ncbw;
-    const int rest = lid / ncbw;
-    c.chunk = rest % a.K;
-    c.seq = rest / a.K;
+    int cbw;
+    if constexpr (kChain) {
+        c.chunk = lid % a.K;
+        const int rest = lid / a.K;
+        cbw = rest % ncbw;
+        c.seq = rest / ncbw;
+    } else {
+        cbw = lid % ncbw;
+        const int rest = lid / ncbw;
+        c.chunk = rest % a.K;
+        c.seq = rest / a.K;
+    }
     c.lane = static_cast<int>(threadIdx.x) & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     c.dir = uni ? 0 : wave & 1;
@@ -829,8 +842,15 @@ __device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCo
 // aggregates of the chunks before it in scan order folded in the carry combine's order and
 // arithmetic (so bit for bit the combine's result). The loads go kFoldBatch chunks at a time, all
 // issued together, clamped to a chunk whose aggregate exists; only the first cnt enter the fold.
+// kCoherent: the aggregates are being written by other workgroups of the same kernel
+// (k_bidir_chain): every load is a device-coherent one (an agent-scope atomic load).
+template <bool kCoherent = false>
 __device__ __forceinline__ void fold_carry(const ScanArgs& a, int dir, int seq, int chunk, int dc, const float (&an)[kN],
                                            float (&h)[kN]) {
+    auto ld = [](const float* p) {
+        if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else return *p;
+    };
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
     const int cnt = dir == 0 ? chunk : a.K - 1 - chunk;  // chunks before this one in scan order
 #pragma unroll
@@ -841,9 +861,9 @@ __device__ __forceinline__ void fold_carry(const ScanArgs& a, int dir, int seq, 
         for (int j = 0; j < kFoldBatch; ++j) {
             const int k = dir == 0 ? min(j0 + j, a.K - 2) : max(a.K - 1 - j0 - j, 1);
             const int64_t slot = base + k;
-            sv[j] = a.dsum[slot * a.Di + dc];
+            sv[j] = ld(a.dsum + slot * a.Di + dc);
 #pragma unroll
-            for (int n = 0; n < kN; ++n) e[j][n] = a.carry[(slot * kN + n) * a.Di + dc];
+            for (int n = 0; n < kN; ++n) e[j][n] = ld(a.carry + (slot * kN + n) * a.Di + dc);
         }
 #pragma unroll
         for (int j = 0; j < kFoldBatch; ++j)
@@ -974,6 +994,144 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
     }
 }
 
+// One-pass chunked scan: the aggregate pass, the fold and the scan of k_chunk_aggregate and
+// k_bidir_scan in one kernel, chunks handing their aggregates to the other chunks of their
+// sequence through the workspace. Each workgroup stages its chunk's rows once, computes the
+// aggregate of its chunk in both directions (the state after the chunk from a zero state, walked
+// against the scan order as in k_chunk_aggregate), publishes it, waits until every chunk before it
+// in scan order has published, folds those aggregates (fold_carry) and runs the scan from the
+// folded state.
+//
+// Publication: a wave stores its aggregate and delta sum with device-coherent stores (agent-scope
+// atomic stores, written through to where every XCD reads them), waits until all of them have
+// completed, and only then stores the dispatch's tag in its tag word; a waiting wave reads the
+// tag words of the aggregates it needs until all hold the tag, and only then issues its
+// device-coherent loads of the aggregates. Both sides order their accesses by waiting for
+// completion, not with agent-scope fences: such a fence writes back or invalidates the whole L2
+// of the XCD, and with thousands of waves publishing that serialises the kernel (it measured
+// several times slower than the two kernels it replaces). The tag is unique to the kernel dispatch (its
+// packet index in its queue, mixed with the queue's address), so tag words left by earlier calls
+// or holding arbitrary bytes never match it: the workspace needs no clearing between calls and no
+// initial contents.
+//
+// Progress: a chunk waits only for the other chunks of its (sequence, channel-block group), whose
+// workgroups have the neighbouring ids (wg_coords<true>), and it publishes before it waits. The
+// hardware starts the workgroups of each XCD in increasing id order, so the chunks of the lowest
+// group not yet complete are the first ones waiting on their XCDs; with room for at least
+// kFoldMaxChunks workgroups per XCD (32 CUs, at least one workgroup each) all of them run at once
+// and complete, and so on group by group. The wait is bounded all the same (kSpinLimit reads,
+// about a second): past it the wave goes on, and its output is unspecified.
+constexpr int kSpinLimit = 1 << 20;
+
+// llvm.amdgcn.dispatch.id: the dispatch packet's index in its queue, which the command processor
+// writes into two SGPRs of every wave it launches.
+extern "C" __device__ uint64_t vimscan_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// A tag unique to this kernel dispatch: the packet index and the queue's address, through the
+// splitmix64 finaliser (a bijection), so that tags of neighbouring dispatches differ in every bit
+// position; never zero.
+__device__ __forceinline__ uint64_t dispatch_tag() {
+    uint64_t v = vimscan_dispatch_id() ^
+                 (reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr()) * 0x9E3779B97F4A7C15ull);
+    v = (v ^ (v >> 30)) * 0xBF58476D1CE4E5B9ull;
+    v = (v ^ (v >> 27)) * 0x94D049BB133111EBull;
+    return (v ^ (v >> 31)) | 1u;
+}
+
+// The tag word of the aggregate of (dir, seq, chunk) for channel block cb.
+__device__ __forceinline__ uint64_t* tag_word(const ScanArgs& a, int dir, int seq, int chunk, int cb) {
+    return a.tags + ((static_cast<int64_t>(dir) * a.nseq + seq) * a.K + chunk) * a.ncb + cb;
+}
+
+// Wait until the aggregates of the chunks before `chunk` in scan order (for this wave's direction
+// and channel block) are published: lane j reads the tag word of the j-th of them (at most
+// kFoldMaxChunks - 1 < 64).
+__device__ __forceinline__ void wait_published(const ScanArgs& a, const WgCoords& c, uint64_t tag) {
+    const int cnt = c.dir == 0 ? c.chunk : a.K - 1 - c.chunk;
+    if (cnt == 0) return;
+    const bool mine = c.lane < cnt;
+    const int k = mine ? (c.dir == 0 ? c.lane : a.K - 1 - c.lane) : c.chunk;
+    const uint64_t* w = tag_word(a, c.dir, c.seq, k, c.cb);
+    for (int it = 0; it < kSpinLimit; ++it) {
+        const bool ready = !mine || __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        if (__all(ready)) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    asm volatile("" ::: "memory");  // the aggregate loads stay after the wait
+}
+
+template <typename IO, bool kGlobalPark, int kVar>
+__global__ __launch_bounds__(256) void k_bidir_chain(ScanArgs a) {
+    constexpr bool kConv = kVar == kWithConv;
+    constexpr int kAggMode = kConv ? kAggregate : kAggRev;
+    constexpr bool kPrime = kVar != kOrdered;
+    // LDS as k_bidir_scan: C and B rows [4][T][16]; in a given order the chunk's order [T]; the
+    // park [subs][T][64] when in LDS
+    extern __shared__ float lds[];
+    const WgCoords c = wg_coords<true>(a, false);
+    const float* lds_c = lds + c.dir * a.T * kN;
+    const float* lds_b = lds + (2 + c.dir) * a.T * kN;
+    const int32_t* lds_ord = reinterpret_cast<const int32_t*>(lds + 4 * a.T * kN);
+    float* lds_park = lds + 4 * a.T * kN + (kVar == kOrdered ? a.T : 0) + c.sub * a.T * kWave;
+    const int len = c.t1 - c.t0;
+    const int half = len >> 1;
+    const int n1 = c.dir == 0 ? half : len - half;  // tokens this wave parks before the barrier
+    // This wave's aggregate is used unless its chunk is the last in scan order; a wave past the
+    // last channel block neither publishes nor waits.
+    const bool live = c.cb < a.ncb;
+    const bool publishes = live && c.chunk != (c.dir == 0 ? a.K - 1 : 0);
+    const uint64_t tag = dispatch_tag();
+    Lane ln;
+    ln.init(a, c.dir, c.dc, kConv);
+    if (kConv) ln.init_conv(a, c.dir, c.dc);
+    Ring<ring_depth(kVar)> rg;
+    if constexpr (kPrime) {
+        if (publishes) prime_ring<IO, kAggMode, false, kVar>(a, c, ln, 0, len, rg);
+    }
+    int form;
+    {
+        const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
+        if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, true);
+        else stage_rows<IO>(a, c, lds, false, true);
+        form = ln.decay_form(a, arow);
+    }
+    __syncthreads();  // the rows are staged
+    if (publishes) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
+        float s = 0.0f;
+        walk_as<IO, kAggMode, false, kVar, kPrime ? kRingPrimed : kRingFull>(form, a, c, ln, nullptr, nullptr, lds_b,
+                                                                            lds_ord, 0, len, s, rg);
+        if (c.valid) {
+            const int64_t slot = (static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk;
+            float* dst = a.carry + slot * kN * a.Di;
+#pragma unroll
+            for (int n = 0; n < kN; ++n)
+                __hip_atomic_store(dst + n * static_cast<int64_t>(a.Di) + c.d, ln.h[n], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.dsum + slot * a.Di + c.d, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every store above has completed
+        if (c.lane == 0)
+            __hip_atomic_store(tag_word(a, c.dir, c.seq, c.chunk, c.cb), tag, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (kPrime) prime_ring<IO, kPark, kGlobalPark, kVar>(a, c, ln, 0, n1, rg);
+    if (live) {
+        wait_published(a, c, tag);
+        const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
+        fold_carry<true>(a, c.dir, c.seq, c.chunk, c.dc, arow.r, ln.h);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
+    }
+    float unused = 0.0f;
+    walk_as<IO, kPark, kGlobalPark, kVar, kPrime ? kRingPrimed : kRingFull>(form, a, c, ln, lds_park, lds_c, lds_b,
+                                                                              lds_ord, 0, n1, unused, rg);
+    __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
+    walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, n1, len, unused, rg);
+}
+
 // Carry combine: for each (direction, sequence, state n, channel) fold the chunk aggregates in
 // scan order; carry[chunk] is replaced by the state entering that chunk. The fold is the
 // associative operator of the linear recurrence: (P1, e1) then (P2, e2) -> (P1 P2, P2 e1 + e2),
@@ -1050,9 +1208,17 @@ void launch_scan(const ScanArgs& a, const Plan& p, hipStream_t s, bool carry) {
     else hipLaunchKernelGGL((k_bidir_scan<IO, false, kGlobalPark, kVar>), grid, block, lds, s, a);
 }
 
+template <typename IO, bool kGlobalPark, int kVar>
+void launch_chain(const ScanArgs& a, const Plan& p, hipStream_t s) {
+    const size_t lds =
+        (4 * p.T * kN + (kVar == kOrdered ? p.T : 0) + (kGlobalPark ? 0 : p.subs * p.T * kWave)) * sizeof(float);
+    hipLaunchKernelGGL((k_bidir_chain<IO, kGlobalPark, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
+                       lds, s, a);
+}
+
 template <typename IO, int kVar>
 int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (p.K > 1) {
+    if (p.K > 1 && !p.chain) {
         const size_t lds = (static_cast<size_t>(p.uni ? 1 : 2) * p.T * kN + (kVar == kOrdered ? p.T : 0)) * sizeof(float);
         hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
                            lds, s, a);
@@ -1067,6 +1233,9 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
                                         lds, s, a);
         else hipLaunchKernelGGL((k_fwd_scan<IO, false>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), lds,
                                 s, a);
+    } else if (p.chain) {
+        if (p.park_global) launch_chain<IO, true, kVar>(a, p, s);
+        else launch_chain<IO, false, kVar>(a, p, s);
     } else if (p.park_global) {
         launch_scan<IO, true, kVar>(a, p, s, p.K > 1);
     } else {
@@ -1148,6 +1317,7 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.carry = p.K > 1 ? reinterpret_cast<float*>(ws) : nullptr;
     a.dsum = p.K > 1 ? reinterpret_cast<float*>(ws + p.off_dsum) : nullptr;
     a.parkg = p.park_global ? reinterpret_cast<float*>(ws + p.off_park) : nullptr;
+    a.tags = p.chain ? reinterpret_cast<uint64_t*>(ws + p.off_tags) : nullptr;
     a.Lp = static_cast<int>(p.Lp);
     a.Di = static_cast<int>(launch->d_inner);
     a.nseq = static_cast<int>(p.nseq);

@@ -62,18 +62,21 @@ def test_plans_for_the_workloads(lib):
     assert folded["park_in_workspace"] == 0 and folded["kernels"] == 1
     assert folded["workspace_bytes"] == 0
     hi = plans["highres_b8_l1025_d768_bf16"]
-    assert hi["chunks"] > 1 and hi["kernels"] == 2 and hi["workspace_bytes"] > 0
+    # chunked, one kernel: the chunks hand their aggregates over through the workspace (carries,
+    # delta sums and a tag word per direction, sequence, chunk and channel block)
+    assert hi["chunks"] > 1 and hi["kernels"] == 1 and hi["workspace_bytes"] > 0
     assert hi["chunk_len"] * hi["chunks"] >= 1025 > hi["chunk_len"] * (hi["chunks"] - 1)
     assert hi["park_in_workspace"] == 0
     carry = 2 * 8 * hi["chunks"] * 16 * 768 * 4
     dsum = 2 * 8 * hi["chunks"] * 768 * 4
-    assert hi["workspace_bytes"] == carry + dsum
+    tags = 2 * 8 * hi["chunks"] * 12 * 8
+    assert hi["workspace_bytes"] == carry + dsum + tags
     # Vim-Ti in one pass would be 192 workgroups, one per CU at most: it is cut into 4 chunks of 50
-    # (768 workgroups), with the carries and delta sums in the workspace and the park in LDS
+    # (768 workgroups), with the carries, delta sums and tags in the workspace and the park in LDS
     ti = binding.launch_info(64, 197, 384, 16, 0, "f32")
-    assert (ti["chunk_len"], ti["chunks"], ti["workgroups"], ti["kernels"]) == (50, 4, 768, 2)
-    carry, dsum = 2 * 64 * 4 * 16 * 384 * 4, 2 * 64 * 4 * 384 * 4
-    assert ti["park_in_workspace"] == 0 and ti["workspace_bytes"] == carry + dsum
+    assert (ti["chunk_len"], ti["chunks"], ti["workgroups"], ti["kernels"]) == (50, 4, 768, 1)
+    carry, dsum, tags = 2 * 64 * 4 * 16 * 384 * 4, 2 * 64 * 4 * 384 * 4, 2 * 64 * 4 * 6 * 8
+    assert ti["park_in_workspace"] == 0 and ti["workspace_bytes"] == carry + dsum + tags
     one_pass = binding.launch_info(64, 197, 384, 16, 0, "f32", chunk_len=197)
     assert one_pass["kernels"] == 1 and one_pass["workspace_bytes"] == one_pass["workgroups"] * 2 * 197 * 64 * 4
     # a forced chunk length is honoured and capped at 256 tokens
@@ -83,12 +86,13 @@ def test_plans_for_the_workloads(lib):
 
 def test_chunk_count_follows_the_cost_model():
     """The bidirectional plan takes the chunk count of least modelled time (plan.cpp plan_cost:
-    scan rounds, aggregate pass, fold or combine, kernel launches), fitted to a forced-chunk sweep
-    on an MI355X; forward only keeps its rule. Choices below were each measured against every
-    forced chunk count (bench.py --chunk-sweep): Vim-Ti 4 x 50 (53.5 us, best of 15), the
-    high-res batch 16 x 65 (63.7 us, best), one 1025-token sequence 41 x 25 (31.8 us; best 31.8),
-    a 4097-token pair 64 x 65 (69.8 us, best), a 16-image Vim-S shard 8 x 25 (33.9 us; best 32.9
-    at 5 x 40), the tiny case 9 x 8 (12.8 us; one pass 22.4 us)."""
+    scan rounds, the one-pass kernel's aggregate walk and hand-over up to 16 chunks, the aggregate
+    pass, combine and launches past that), fitted to a forced-chunk sweep on an MI355X; forward
+    only keeps its rule. Choices below were each measured against every forced chunk count
+    (bench.py --chunk-sweep): Vim-Ti 4 x 50 (47.7 us, best of 15), the high-res batch 16 x 65
+    (62.6 us, best), one 1025-token sequence 41 x 25 (32.0 us; best 31.8 at 40 x 26), a 4097-token
+    pair 64 x 65 (69.3 us, best), a 16-image Vim-S shard 5 x 40 (31.7 us, best), 8 x 577 tokens
+    10 x 58 (43.6 us, best), the tiny case 6 x 11 (12.3 us; best 11.8 at 9 x 8; one pass 22 us)."""
     def plan(*shape, fwd=False):
         i = binding.launch_info(*shape, forward_only=fwd)
         return i["chunk_len"], i["chunks"], i["workgroups"]
@@ -96,8 +100,9 @@ def test_chunk_count_follows_the_cost_model():
     assert plan(8, 1025, 768, 16, 0, "bf16")[:2] == (65, 16)
     assert plan(1, 1025, 768, 16, 0, "bf16")[:2] == (25, 41)
     assert plan(2, 4097, 768, 16, 0, "bf16")[:2] == (65, 64)
-    assert plan(16, 197, 768, 16, 0, "bf16")[:2] == (25, 8)
-    assert plan(2, 65, 32, 16, 0, "f32")[:2] == (8, 9)
+    assert plan(16, 197, 768, 16, 0, "bf16")[:2] == (40, 5)
+    assert plan(8, 577, 768, 16, 0, "bf16")[:2] == (58, 10)
+    assert plan(2, 65, 32, 16, 0, "f32")[:2] == (11, 6)
     # enough workgroups for the chip: one pass (Vim-S, the folded stream)
     assert plan(128, 197, 768, 16, 0, "bf16")[:2] == (197, 1)
     assert plan(1, 13056, 1536, 16, 51, "bf16")[:2] == (51, 1)
@@ -110,11 +115,12 @@ def test_chunk_count_follows_the_cost_model():
         for fwd in (False, True):
             T, K, _ = plan(*shape, 16, 0, "bf16", fwd=fwd)
             assert 8 <= T <= 256 and K == -(-shape[1] // T)
-    # up to 16 chunks the scan workgroups fold the aggregates themselves: no carry-combine kernel
-    assert binding.launch_info(16, 197, 768, 16, 0, "bf16")["kernels"] == 2
-    assert binding.launch_info(8, 1025, 768, 16, 0, "bf16")["kernels"] == 2
+    # up to 16 chunks one kernel computes, hands over and folds the aggregates itself (no aggregate
+    # or carry-combine kernel); past that the aggregate pass, the combine and the scan
+    assert binding.launch_info(16, 197, 768, 16, 0, "bf16")["kernels"] == 1
+    assert binding.launch_info(8, 1025, 768, 16, 0, "bf16")["kernels"] == 1
     assert [binding.launch_info(1, 256, 64, 16, 0, "f32", chunk_len=t)["kernels"] for t in (256, 128, 16, 15)] == \
-        [1, 2, 2, 3]
+        [1, 1, 1, 3]
     # the element limit: chunks of at most 256 tokens, many rounds of workgroups, the combine kernel
     T, K, _ = plan(1, 2097151, 1024, 16, 0, "bf16")
     assert T <= 256 and K == -(-2097151 // T) and binding.launch_info(1, 2097151, 1024, 16, 0, "bf16")["kernels"] == 3

@@ -13,11 +13,13 @@ auxiliary swap, and the three NC-SSD passes -- this file recomputes, from the li
   and every offset formed against them inside the range (out-of-range buffer offsets would be
   dropped by the hardware, so they would lose data rather than fault: they must not occur either);
 * LDS addresses against the dynamic LDS size of the launch and the 160 KB of a CU;
-* the workspace layout against vimscan_workspace_bytes, and the XCD remap of workgroup ids as a
-  permutation of the grid.
+* the workspace layout against vimscan_workspace_bytes, the XCD remap of workgroup ids as a
+  permutation of the grid, and the one-pass chunked kernel's workgroup order (a bijection onto
+  sequence x channel-block group x chunk, chunk fastest) and tag words.
 
 The index formulas restate the kernel code (vimscan.hip: wg_coords, stage_rows,
-stage_rows_ordered, walk, fold_carry, k_chunk_aggregate, k_carry_combine, k_aux_swap; ncssd.hip:
+stage_rows_ordered, walk, fold_carry, k_chunk_aggregate, k_bidir_chain, tag_word, wait_published,
+k_carry_combine, k_aux_swap; ncssd.hip:
 state_tiles, load_c, out_tiles, k_ncssd_state, k_ncssd_reduce, k_ncssd_out). Extremes over lanes
 and steps are taken analytically where an index is monotone in them (as every one is), so the
 element-limit shape (65,536 workgroups) replays in well under a second.
@@ -80,18 +82,22 @@ def scan_plan(B, L, Di, io, seg, chunk, uni, ordered=False):
     assert p["workgroups"] == p["nseq"] * p["K"] * p["wpc"], p
     assert p["K"] == ceil_div(p["Lp"], p["T"]) and p["T"] <= 256
     p["fold"] = 1 < p["K"] <= FOLD_MAX
+    p["chain"] = p["fold"] and not uni             # one kernel: k_bidir_chain
+    assert info["kernels"] == (1 if p["K"] == 1 or p["chain"] else 2 if p["fold"] else 3), info
     ndir = 1 if uni else 2
     f = 4
     carry = ndir * p["nseq"] * p["K"] * N * Di * f if p["K"] > 1 else 0
     dsum = ndir * p["nseq"] * p["K"] * Di * f if p["K"] > 1 else 0
     park = p["workgroups"] * p["subs"] * p["T"] * WAVE * f if p["park_in_workspace"] else 0
+    tags = ndir * p["nseq"] * p["K"] * p["ncb"] * 8 if p["chain"] else 0
     off_dsum = round_up(carry, 256)
     off_park = round_up(off_dsum + dsum, 256)
-    ws = off_park + park if carry + dsum + park > 0 else 0
+    off_tags = round_up(off_park + park, 256)
+    ws = off_tags + tags if carry + dsum + park + tags > 0 else 0
     assert ws == info["workspace_bytes"], (ws, info)
     assert bool(p["park_in_workspace"]) == (not uni and p["T"] * WAVE * 4 > 20 * 1024)
-    p.update(ndir=ndir, carry_floats=carry // f, dsum_floats=dsum // f, park_floats=park // f,
-             off_dsum=off_dsum, off_park=off_park, ws=ws)
+    p.update(ndir=ndir, carry_floats=carry // f, dsum_floats=dsum // f, park_floats=park // f, tag_words=tags // 8,
+             off_dsum=off_dsum, off_park=off_park, off_tags=off_tags, ws=ws)
     return p
 
 
@@ -99,13 +105,23 @@ def coords(p, uni, waves):
     """wg_coords for every (workgroup, wave): arrays over hardware ids bid (grid order) x waves."""
     grid = p["workgroups"]
     bid = np.arange(grid, dtype=np.int64)
-    lid = xcd_remap(bid, grid)
-    assert np.array_equal(np.sort(lid), bid), "the XCD remap is not a permutation of the grid"
     ncbw = p["wpc"]
-    cbw = lid % ncbw
-    rest = lid // ncbw
-    chunk = rest % p["K"]
-    seq = rest // p["K"]
+    if p.get("chain"):
+        # k_bidir_chain: hardware order, chunk fastest, then the channel-block group
+        lid = bid
+        chunk = lid % p["K"]
+        rest = lid // p["K"]
+        cbw = rest % ncbw
+        seq = rest // ncbw
+        key = (seq * ncbw + cbw) * p["K"] + chunk
+        assert np.array_equal(np.sort(key), bid), "chain workgroups do not cover sequence x group x chunk once"
+    else:
+        lid = xcd_remap(bid, grid)
+        assert np.array_equal(np.sort(lid), bid), "the XCD remap is not a permutation of the grid"
+        cbw = lid % ncbw
+        rest = lid // ncbw
+        chunk = rest % p["K"]
+        seq = rest // p["K"]
     wave = np.arange(waves, dtype=np.int64)
     c = {}
     c["lid"] = lid[:, None]
@@ -154,7 +170,7 @@ def replay_scan(B, L, Di, io, seg=0, chunk=0, variant="plain", taps=4):
     scan_lds = (regions * T * N + (T if ordered else 0) + (p["subs"] * T * WAVE if lds_park else 0)) * 4
     agg_lds = (p["ndir"] * T * N + (T if ordered else 0)) * 4
     ck.add("scan kernel LDS bytes", 0, scan_lds - 1, LDS_PER_CU)
-    if K > 1:
+    if K > 1 and not p["chain"]:
         ck.add("aggregate kernel LDS bytes", 0, agg_lds - 1, LDS_PER_CU)
     # staged rows: region r, local row < len, 16 values; order copy after the rows; the LDS park
     ck.add("LDS row staging (floats)", 0, (regions - 1) * T * N + c["len"] * N - 1, scan_lds // 4)
@@ -229,6 +245,22 @@ def replay_scan(B, L, Di, io, seg=0, chunk=0, variant="plain", taps=4):
             ck.add("fold slot", base + lo_k, base + hi_k, p["ndir"] * nseq * K)
             ck.add("fold carry elements", ((base + lo_k) * N) * Di + dlo, ((base + hi_k) * N + N - 1) * Di + dhi,
                    p["carry_floats"])
+        if p["chain"]:
+            # k_bidir_chain: a live wave (cb < ncb) publishes tag_word(dir, seq, chunk, cb) and
+            # waits on the words of chunks 0..cnt-1 (forward) or K-cnt..K-1 (backward)
+            live = c["cb"] < p["ncb"]
+            cnt = np.where(c["dir"] == 0, c["chunk"], K - 1 - c["chunk"])
+            fwd = c["dir"] == 0
+            k_lo = np.where(cnt > 0, np.where(fwd, 0, K - cnt), c["chunk"])
+            k_hi = np.where(cnt > 0, np.where(fwd, cnt - 1, K - 1), c["chunk"])
+            word = lambda k: ((c["dir"] * nseq + c["seq"]) * K + k) * p["ncb"] + c["cb"]
+            cb_live = np.where(live, c["cb"], 0)
+            ck.add("live channel block", cb_live, cb_live, p["ncb"])
+            ck.add("published tag word", np.where(live, word(c["chunk"]), 0), np.where(live, word(c["chunk"]), 0),
+                   p["tag_words"])
+            ck.add("awaited tag words", np.where(live, word(k_lo), 0), np.where(live, word(k_hi), 0), p["tag_words"])
+            ck.add("lanes watching tag words", 0, np.max(cnt), WAVE)
+            ck.add("tags inside the workspace (bytes)", p["off_tags"], p["off_tags"] + p["tag_words"] * 8 - 1, p["ws"])
         else:
             # k_carry_combine: grid (ncb * ndir * nseq, 4), 256 threads = 64 channels x 4 states
             gx = p["ncb"] * p["ndir"] * nseq
@@ -354,14 +386,15 @@ def test_ncssd_shapes():
 
 def test_a_planted_index_error_is_caught(monkeypatch):
     """The replay itself: an index one past a buffer fails, and so do plans whose workspace regions
-    are one element short of what the kernels address (a park, the carries, the delta sums)."""
+    are one element short of what the kernels address (a park, the carries, the delta sums, the
+    one-pass kernel's tag words)."""
     ck = Checks("planted")
     ck.add("one past the end", 0, 10, 10)
     with pytest.raises(AssertionError):
         ck.verify()
     real = scan_plan
     for key, shape in (("park_floats", (2, 400, 64, "bf16", 0, 150)), ("carry_floats", (2, 1025, 64, "bf16", 0, 0)),
-                       ("dsum_floats", (1, 40000, 64, "f32", 0, 0))):
+                       ("dsum_floats", (1, 40000, 64, "f32", 0, 0)), ("tag_words", (2, 400, 64, "bf16", 0, 50))):
         B, L, Di, io, seg, chunk = shape
         assert real(B, L, Di, io, seg, chunk, False)[key] > 0   # the region exists in this plan
 
