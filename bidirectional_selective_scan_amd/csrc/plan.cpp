@@ -83,8 +83,10 @@ int64_t uni_chunks(const ScanPlan* p, int io_dtype) {
 //  * the scan: T token steps per workgroup, in rounds of resident_wgs;
 //  * with 2..kFoldMaxChunks chunks, the one-pass kernel's own aggregate walk (no readout, walked
 //    against the scan order) at 0.296 of a scan step per token plus 62.9 for its staging, stores
-//    and hand-over, in the same rounds, and 2.66 per chunk of the sequence per round for the wait
-//    on the other chunks and the fold of their aggregates;
+//    and hand-over, in the same rounds, and 2.4 per chunk of the sequence per round for the wait
+//    on the other chunks and the fold of their aggregates (the fits gave 2.7-2.8, with the tiny
+//    case's 6 and 9 chunks 4% apart; 2.4 picks the measured best chunk count of all ten shapes in
+//    two sweeps);
 //  * past kFoldMaxChunks, the separate aggregate pass: 0.139 of a scan step per token plus 109.6,
 //    at up to 5 workgroups per CU; the combine kernel: 3.86 + 14.0 per 16 chunks; 32.2 for each of
 //    the two kernels after the first (launch and drain).
@@ -98,7 +100,7 @@ double plan_cost(const ScanPlan* p, int io_dtype, int64_t K) {
     const double t = static_cast<double>(T);
     double c = t * rs;
     if (K > 1 && K <= kFoldMaxChunks) {
-        c += 0.296 * (t + 62.9) * rs + 2.66 * static_cast<double>(K * nr);
+        c += 0.296 * (t + 62.9) * rs + 2.4 * static_cast<double>(K * nr);
     } else if (K > kFoldMaxChunks) {
         c += 0.139 * (t + 109.6) * rounds(per_cu, std::min<int64_t>(5, kLdsPerCu / (T * kN * 8 + 1)));
         c += 3.86 + 14.0 * static_cast<double>((K + 15) / 16) + 2 * 32.2;
@@ -204,10 +206,10 @@ int make_scan_plan(const vimscan_launch* l, int64_t seg_len, ScanPlan* p) {
     // With few chunks every scan workgroup folds the aggregates before its chunk itself: no
     // combine kernel, and the carries are written once and read, not rewritten.
     p->fold = p->K > 1 && p->K <= kFoldMaxChunks;
-    // Bidirectional, those plans run as one kernel: every workgroup computes its own chunk's
-    // aggregates, publishes them and folds those of the chunks before it (k_bidir_chain).
-    p->chain = p->fold && !p->uni;
-    p->kernels = (p->K > 1 ? (p->chain ? 1 : p->fold ? 2 : 3) : 1) + (p->swap ? 1 : 0);
+    // Those plans run as one kernel: every workgroup computes its own chunk's aggregates,
+    // publishes them and folds those of the chunks before it (k_bidir_chain, k_fwd_chain).
+    p->chain = p->fold;
+    p->kernels = (p->K > 1 && !p->chain ? 3 : 1) + (p->swap ? 1 : 0);
     p->park_global = !p->uni && p->T * kWave * static_cast<int64_t>(sizeof(float)) > kLdsParkMaxBytes;
     const size_t f = sizeof(float);
     const size_t ndir = p->uni ? 1 : 2;

@@ -18,8 +18,8 @@ constexpr int kN = 16;              // state width
 constexpr int kWave = 64;           // wavefront width on gfx950
 constexpr int kMaxChunk = 256;      // tokens per chunk
 constexpr int kMaxTaps = 4;         // taps of the directional convolution
-// Plans of up to kFoldMaxChunks chunks run without the carry combine kernel: each scan workgroup
-// folds the chunk aggregates before its chunk itself.
+// Plans of up to kFoldMaxChunks chunks run as one kernel: each workgroup computes its chunk's
+// aggregates, hands them to the later chunks and folds the aggregates before its chunk itself.
 constexpr int kFoldMaxChunks = 16;
 // A park larger than this goes to global scratch: in LDS it would cap a CU at fewer than 8
 // workgroups, and the VALU needs several waves per SIMD to issue at full rate.
@@ -40,7 +40,7 @@ struct ScanPlan {
     int64_t nseq, Lp, T, K, ncb, subs, wgs;
     int kernels;
     bool park_global, uni, swap, fold;
-    bool chain;                                // bidirectional with 2..kFoldMaxChunks chunks: one kernel
+    bool chain;                                // 2..kFoldMaxChunks chunks: one kernel
     size_t ws;                                 // total scratch bytes
     size_t off_dsum, off_park, off_tags;      // byte offsets of the regions after the carries
 };

@@ -27,12 +27,15 @@
 //  * Software pipelining: the state-independent part of a token (softplus, delta*x, the 16
 //    transitions exp(delta*A)) is computed one token ahead, so it overlaps the dependent state
 //    update of the current token; loads run several tokens ahead.
-//  * Long sequences are cut into chunks (the associative form of the linear recurrence):
-//    pass 1 computes, per chunk and direction, the local end state from zero and the sum of
-//    delta over the chunk (the chunk's transition product is exp(A * sum delta)); a small
-//    combine kernel folds these left-to-right (forward) and right-to-left (backward) into the
-//    state entering every chunk; pass 2 re-runs each chunk from its incoming state with the
-//    readout. Carries live in the caller's workspace.
+//  * Long sequences are cut into chunks (the associative form of the linear recurrence): per
+//    chunk and direction the local end state from zero and the sum of delta over the chunk (the
+//    chunk's transition product is exp(A * sum delta)) -- the chunk aggregate; folded in scan
+//    order they give the state entering every chunk, from which the chunk is scanned with the
+//    readout. Up to kFoldMaxChunks chunks per sequence (bidirectional) this is one kernel: each
+//    workgroup computes its own chunk's aggregates, hands them to the other chunks of its
+//    sequence through the workspace (k_bidir_chain, k_fwd_chain) and folds the ones it receives.
+//    Beyond that an aggregate pass, a combine kernel and the scan run as separate kernels.
+//    Carries live in the caller's workspace.
 //  * delta is kept in log2 units (softplus * log2 e), so the transitions are the hardware exp2
 //    of delta2 * A; the state is then scaled by log2(e), which the C rows undo (they are staged
 //    as C * ln 2). When a channel's A row is an arithmetic progression in n, the 16 transitions
@@ -182,13 +185,12 @@ struct ScanArgs {
     int conv_k;          // taps, 1..kMaxTaps; 0 without the convolution
     int uni;             // 1: forward only (vimscan_fwd): every wave of a workgroup is a channel block
     const int32_t* order;  // kOrdered: [nseq][Lp] the token each scan step visits (vimscan_bidir_order_fwd)
-    int fold;              // chunked: 1 when each scan workgroup folds the chunk aggregates itself
-    uint64_t* tags;        // one-pass chunked (k_bidir_chain): [dir][seq][chunk][ncb] publication tags; else null
+    uint64_t* tags;        // one-pass chunked (k_bidir_chain, k_fwd_chain): [dir][seq][chunk][ncb] tags; else null
 };
 
 // The directional convolution carries kMaxTaps taps (a layer with fewer taps is run with the
-// missing ones at zero). Plans of up to kFoldMaxChunks chunks run without the carry combine
-// kernel: each scan workgroup folds the aggregates before its chunk itself, kFoldBatch chunks per
+// missing ones at zero). Plans of up to kFoldMaxChunks chunks run as one kernel whose workgroups
+// fold the aggregates of the chunks before theirs themselves (fold_carry), kFoldBatch chunks per
 // round of loads.
 constexpr int kFoldBatch = 4;
 
@@ -842,15 +844,12 @@ __device__ __forceinline__ void stage_rows_ordered(const ScanArgs& a, const WgCo
 // aggregates of the chunks before it in scan order folded in the carry combine's order and
 // arithmetic (so bit for bit the combine's result). The loads go kFoldBatch chunks at a time, all
 // issued together, clamped to a chunk whose aggregate exists; only the first cnt enter the fold.
-// kCoherent: the aggregates are being written by other workgroups of the same kernel
-// (k_bidir_chain): every load is a device-coherent one (an agent-scope atomic load).
-template <bool kCoherent = false>
+// The aggregates are written by other workgroups of the same kernel (k_bidir_chain,
+// k_fwd_chain): every load is a device-coherent one (an agent-scope atomic load), issued after
+// wait_published.
 __device__ __forceinline__ void fold_carry(const ScanArgs& a, int dir, int seq, int chunk, int dc, const float (&an)[kN],
                                            float (&h)[kN]) {
-    auto ld = [](const float* p) {
-        if constexpr (kCoherent) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else return *p;
-    };
+    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
     const int64_t base = (static_cast<int64_t>(dir) * a.nseq + seq) * a.K;
     const int cnt = dir == 0 ? chunk : a.K - 1 - chunk;  // chunks before this one in scan order
 #pragma unroll
@@ -900,9 +899,7 @@ __global__ __launch_bounds__(256) void k_bidir_scan(ScanArgs a) {
     const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
     if constexpr (kVar == kOrdered) stage_rows_ordered<IO>(a, c, lds, true);
     else stage_rows<IO>(a, c, lds, false, true);
-    if (kCarry && a.fold) {
-        fold_carry(a, c.dir, c.seq, c.chunk, c.dc, arow.r, ln.h);
-    } else if (kCarry) {
+    if (kCarry) {
         const float* src = a.carry + ((static_cast<int64_t>(c.dir) * a.nseq + c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = src[n * static_cast<int64_t>(a.Di) + c.dc];
@@ -933,9 +930,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(ScanArgs a) {
     prime_ring<IO, kOut, false, kPlain>(a, c, ln, 0, len, rg);
     const Lane::ARow arow = ln.load_arow(a, 0, c.dc);
     stage_rows<IO>(a, c, lds, true, true);
-    if (kCarry && a.fold) {
-        fold_carry(a, 0, c.seq, c.chunk, c.dc, arow.r, ln.h);
-    } else if (kCarry) {
+    if (kCarry) {
         const float* src = a.carry + (static_cast<int64_t>(c.seq) * a.K + c.chunk) * kN * a.Di;
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = src[n * static_cast<int64_t>(a.Di) + c.dc];
@@ -1120,7 +1115,7 @@ __global__ __launch_bounds__(256) void k_bidir_chain(ScanArgs a) {
     if (live) {
         wait_published(a, c, tag);
         const Lane::ARow arow = ln.load_arow(a, c.dir, c.dc);
-        fold_carry<true>(a, c.dir, c.seq, c.chunk, c.dc, arow.r, ln.h);
+        fold_carry(a, c.dir, c.seq, c.chunk, c.dc, arow.r, ln.h);
     } else {
 #pragma unroll
         for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
@@ -1130,6 +1125,60 @@ __global__ __launch_bounds__(256) void k_bidir_chain(ScanArgs a) {
                                                                               lds_ord, 0, n1, unused, rg);
     __syncthreads();  // the park is complete (the barrier also orders the global park's stores)
     walk_as<IO, kFinish, kGlobalPark, kVar>(form, a, c, ln, lds_park, lds_c, lds_b, lds_ord, n1, len, unused, rg);
+}
+
+// Forward-only one-pass chunked scan (vimscan_fwd with 2..kFoldMaxChunks chunks): k_bidir_chain's
+// aggregate walk, hand-over and fold in front of k_fwd_scan's walk; every wave a channel block.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_fwd_chain(ScanArgs a) {
+    extern __shared__ float lds[];  // the chunk's C rows [T][16], then its B rows [T][16]
+    const WgCoords c = wg_coords<true>(a, true);
+    const int len = c.t1 - c.t0;
+    const bool live = c.cb < a.ncb;
+    const bool publishes = live && c.chunk != a.K - 1;
+    const uint64_t tag = dispatch_tag();
+    Lane ln;
+    ln.init(a, 0, c.dc, true);
+    Ring<ring_depth(kPlain)> rg;
+    if (publishes) prime_ring<IO, kAggRev, false, kPlain>(a, c, ln, 0, len, rg);
+    int form;
+    {
+        const Lane::ARow arow = ln.load_arow(a, 0, c.dc);
+        stage_rows<IO>(a, c, lds, true, true);
+        form = ln.decay_form(a, arow);
+    }
+    __syncthreads();  // the rows are staged
+    if (publishes) {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
+        float s = 0.0f;
+        walk_as<IO, kAggRev, false, kPlain, kRingPrimed>(form, a, c, ln, nullptr, nullptr, lds + a.T * kN, nullptr, 0,
+                                                        len, s, rg);
+        if (c.valid) {
+            const int64_t slot = static_cast<int64_t>(c.seq) * a.K + c.chunk;
+            float* dst = a.carry + slot * kN * a.Di;
+#pragma unroll
+            for (int n = 0; n < kN; ++n)
+                __hip_atomic_store(dst + n * static_cast<int64_t>(a.Di) + c.d, ln.h[n], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.dsum + slot * a.Di + c.d, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every store above has completed
+        if (c.lane == 0)
+            __hip_atomic_store(tag_word(a, 0, c.seq, c.chunk, c.cb), tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    prime_ring<IO, kOut, false, kPlain>(a, c, ln, 0, len, rg);
+    if (live) {
+        wait_published(a, c, tag);
+        const Lane::ARow arow = ln.load_arow(a, 0, c.dc);
+        fold_carry(a, 0, c.seq, c.chunk, c.dc, arow.r, ln.h);
+    } else {
+#pragma unroll
+        for (int n = 0; n < kN; ++n) ln.h[n] = 0.0f;
+    }
+    float unused = 0.0f;
+    walk_as<IO, kOut, false, kPlain, kRingPrimed>(form, a, c, ln, nullptr, lds, lds + a.T * kN, nullptr, 0, len,
+                                                  unused, rg);
 }
 
 // Carry combine: for each (direction, sequence, state n, channel) fold the chunk aggregates in
@@ -1223,13 +1272,15 @@ int launch_all(const ScanArgs& a, const Plan& p, hipStream_t s, hipEvent_t ev0, 
         hipLaunchKernelGGL((k_chunk_aggregate<IO, kVar>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
                            lds, s, a);
         const dim3 cgrid(static_cast<unsigned>(p.ncb * (p.uni ? 1 : 2) * p.nseq), 4);
-        if (!p.fold) hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(k_carry_combine, cgrid, dim3(256), 0, s, a);
     }
     const bool timed = ev0 != nullptr && ev1 != nullptr;
     if (timed && hipEventRecord(ev0, s) != hipSuccess) return VIMSCAN_ERR_HIP;
     if (p.uni) {
         const size_t lds = 2 * static_cast<size_t>(p.T) * kN * sizeof(float);
-        if (p.K > 1) hipLaunchKernelGGL((k_fwd_scan<IO, true>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
+        if (p.chain) hipLaunchKernelGGL((k_fwd_chain<IO>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
+                                        lds, s, a);
+        else if (p.K > 1) hipLaunchKernelGGL((k_fwd_scan<IO, true>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)),
                                         lds, s, a);
         else hipLaunchKernelGGL((k_fwd_scan<IO, false>), dim3(static_cast<unsigned>(p.wgs)), dim3(wg_threads(p)), lds,
                                 s, a);
@@ -1325,7 +1376,6 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
     a.K = static_cast<int>(p.K);
     a.ncb = static_cast<int>(p.ncb);
     a.subs = static_cast<int>(p.subs);
-    a.fold = p.fold ? 1 : 0;
     a.general = (launch->flags & VIMSCAN_FLAG_GENERAL_DECAY) ? 1 : 0;
     a.cw[0] = conv ? conv->w_f : nullptr;
     a.cw[1] = conv ? conv->w_b : nullptr;

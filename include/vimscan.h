@@ -101,7 +101,9 @@ typedef struct vimscan_launch {
                                capped at 256 (a value >= the sequence length gives a single
                                pass for sequences of up to 256 tokens) */
     void* workspace;        /* device scratch of at least vimscan_workspace_bytes() bytes;
-                               may be NULL when that size is 0 */
+                               may be NULL when that size is 0. Its contents on entry do not
+                               matter (no clearing needed); calls that can overlap in time must
+                               not share one */
     size_t workspace_bytes; /* size of workspace */
     void* stream;           /* hipStream_t to queue the work on; NULL = the null stream */
     void* scan_events[2];   /* optional pair of hipEvent_t created by the caller: when both are
@@ -140,15 +142,20 @@ typedef struct vimscan_plan {
     int64_t chunk_len;      /* tokens per chunk */
     int64_t chunks;         /* chunks per sequence; 1 = single pass (no chunk carries) */
     int64_t workgroups;     /* workgroups of the main scan kernel */
-    int32_t kernels;        /* kernels launched per call: the main scan, plus 1 when chunked
-                               (chunk aggregates), plus 1 more beyond 16 chunks per sequence
-                               (carry combine; up to 16 the scan workgroups fold the aggregates
-                               themselves), plus 1 with VIMSCAN_FLAG_AUX_SWAP */
+    int32_t kernels;        /* kernels launched per call: 1 for a single pass and, in both
+                               directions, for 2..16 chunks per sequence (one kernel computes
+                               each chunk's aggregate, hands it to the later chunks through the
+                               workspace and folds those it receives); past 16 chunks 3 (chunk
+                               aggregates, carry combine, scan); forward only 2 for 2..16 chunks
+                               (aggregates, scan folding them); plus 1 with
+                               VIMSCAN_FLAG_AUX_SWAP */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */
     size_t workspace_bytes; /* scratch this call needs: chunk carries and delta sums when
-                               chunks > 1, and chunk_len*64*4 bytes per wave pair when
-                               park_in_workspace (0: no workspace needed) */
+                               chunks > 1, chunk_len*64*4 bytes per wave pair when
+                               park_in_workspace, and 8 bytes per (direction, sequence, chunk,
+                               64-channel block) of hand-over tags for the one-kernel chunked
+                               scan (0: no workspace needed) */
 } vimscan_plan;
 
 /*
@@ -263,8 +270,9 @@ int vimscan_ncssd_plan(const vimscan_launch* launch, int64_t seg_len, vimscan_pl
  * 77.5 MB park included). The array belongs to the current HIP device: its address is looked up
  * (hipGetSymbolAddress) on the first call on each device, which must therefore be current; the
  * call allocates nothing (no hipMalloc, hipFree or allocating library routine). The array keeps
- * the last call's contents; no part of the scan reads scratch it has not written in the same
- * call. Calls on one GPU share its array: two calls that can overlap in time on the same GPU
+ * the last call's contents; the scan uses no scratch value it has not written in the same call
+ * (the one-kernel chunked scan reads hand-over tags that earlier calls left only to see that they
+ * are not its own). Calls on one GPU share its array: two calls that can overlap in time on the same GPU
  * (different streams without an ordering between them) race on it and give undefined results;
  * calls on one stream are ordered and safe.
  */

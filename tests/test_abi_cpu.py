@@ -89,10 +89,10 @@ def test_chunk_count_follows_the_cost_model():
     scan rounds, the one-pass kernel's aggregate walk and hand-over up to 16 chunks, the aggregate
     pass, combine and launches past that), fitted to a forced-chunk sweep on an MI355X; forward
     only keeps its rule. Choices below were each measured against every forced chunk count
-    (bench.py --chunk-sweep): Vim-Ti 4 x 50 (47.7 us, best of 15), the high-res batch 16 x 65
-    (62.6 us, best), one 1025-token sequence 41 x 25 (32.0 us; best 31.8 at 40 x 26), a 4097-token
-    pair 64 x 65 (69.3 us, best), a 16-image Vim-S shard 5 x 40 (31.7 us, best), 8 x 577 tokens
-    10 x 58 (43.6 us, best), the tiny case 6 x 11 (12.3 us; best 11.8 at 9 x 8; one pass 22 us)."""
+    (bench.py --chunk-sweep): Vim-Ti 4 x 50 (46.6 us, best of 15), the high-res batch 16 x 65
+    (62.5 us, best), one 1025-token sequence 41 x 25 (31.7 us; best 31.5 at 40 x 26), a 4097-token
+    pair 64 x 65 (67.1 us, best), a 16-image Vim-S shard 5 x 40 (31.7 us, best), 8 x 577 tokens
+    10 x 58 (43.4 us, best), the tiny case 9 x 8 (11.7 us, best; one pass 22 us)."""
     def plan(*shape, fwd=False):
         i = binding.launch_info(*shape, forward_only=fwd)
         return i["chunk_len"], i["chunks"], i["workgroups"]
@@ -102,7 +102,7 @@ def test_chunk_count_follows_the_cost_model():
     assert plan(2, 4097, 768, 16, 0, "bf16")[:2] == (65, 64)
     assert plan(16, 197, 768, 16, 0, "bf16")[:2] == (40, 5)
     assert plan(8, 577, 768, 16, 0, "bf16")[:2] == (58, 10)
-    assert plan(2, 65, 32, 16, 0, "f32")[:2] == (11, 6)
+    assert plan(2, 65, 32, 16, 0, "f32")[:2] == (8, 9)
     # enough workgroups for the chip: one pass (Vim-S, the folded stream)
     assert plan(128, 197, 768, 16, 0, "bf16")[:2] == (197, 1)
     assert plan(1, 13056, 1536, 16, 51, "bf16")[:2] == (51, 1)
@@ -328,10 +328,15 @@ def test_forward_only_plans(lib):
     s = binding.launch_info(128, 197, 768, 16, 0, "bf16", forward_only=True, aux_swap=True)
     assert s["kernels"] == f["kernels"] + 1
     hi = binding.launch_info(8, 1025, 768, 16, 0, "bf16", forward_only=True)
-    assert hi["chunks"] > 1 and hi["kernels"] == (2 if hi["chunks"] <= 16 else 3)
+    assert hi["chunks"] > 1 and hi["kernels"] == (1 if hi["chunks"] <= 16 else 3)
     carry = 8 * hi["chunks"] * 16 * 768 * 4
     dsum = 8 * hi["chunks"] * 768 * 4
-    assert hi["workspace_bytes"] == carry + dsum
+    tags = 8 * hi["chunks"] * 12 * 8 if hi["chunks"] <= 16 else 0
+    assert hi["workspace_bytes"] == carry + dsum + tags
+    # up to 16 chunks forward only is one kernel too (k_fwd_chain), with its tag words
+    ti = binding.launch_info(64, 197, 384, 16, 0, "f32", forward_only=True)
+    assert (ti["chunks"], ti["kernels"]) == (4, 1)
+    assert ti["workspace_bytes"] == 64 * 4 * 17 * 384 * 4 + 64 * 4 * 6 * 8
 
 
 def _call_fwd(lib, launch, ptrs=None, seg_len=0, y=None):

@@ -18,7 +18,8 @@ auxiliary swap, and the three NC-SSD passes -- this file recomputes, from the li
   sequence x channel-block group x chunk, chunk fastest) and tag words.
 
 The index formulas restate the kernel code (vimscan.hip: wg_coords, stage_rows,
-stage_rows_ordered, walk, fold_carry, k_chunk_aggregate, k_bidir_chain, tag_word, wait_published,
+stage_rows_ordered, walk, fold_carry, k_chunk_aggregate, k_bidir_chain, k_fwd_chain, tag_word,
+wait_published,
 k_carry_combine, k_aux_swap; ncssd.hip:
 state_tiles, load_c, out_tiles, k_ncssd_state, k_ncssd_reduce, k_ncssd_out). Extremes over lanes
 and steps are taken analytically where an index is monotone in them (as every one is), so the
@@ -82,8 +83,8 @@ def scan_plan(B, L, Di, io, seg, chunk, uni, ordered=False):
     assert p["workgroups"] == p["nseq"] * p["K"] * p["wpc"], p
     assert p["K"] == ceil_div(p["Lp"], p["T"]) and p["T"] <= 256
     p["fold"] = 1 < p["K"] <= FOLD_MAX
-    p["chain"] = p["fold"] and not uni             # one kernel: k_bidir_chain
-    assert info["kernels"] == (1 if p["K"] == 1 or p["chain"] else 2 if p["fold"] else 3), info
+    p["chain"] = p["fold"]                         # one kernel: k_bidir_chain / k_fwd_chain
+    assert info["kernels"] == (1 if p["K"] == 1 or p["chain"] else 3), info
     ndir = 1 if uni else 2
     f = 4
     carry = ndir * p["nseq"] * p["K"] * N * Di * f if p["K"] > 1 else 0

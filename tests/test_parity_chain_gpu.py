@@ -10,7 +10,9 @@ What these tests pin down beyond the plain parity tests:
   gives every call its own result bit for bit (no call reads another call's aggregates);
 * two streams, each with its own workspace, interleaved, likewise;
 * the plan: one kernel per call, a tag word per (direction, sequence, chunk, channel block) in the
-  workspace after the other regions.
+  workspace after the other regions;
+* the same for the forward-only scan (vimscan_fwd), whose chunked plans of up to 16 chunks are one
+  kernel as well.
 Shapes: ragged last chunks, a ragged last channel block and an odd channel-block count (a spare
 wave that neither publishes nor waits), 2 to 16 chunks, fp32 and bf16 io."""
 import numpy as np
@@ -113,3 +115,31 @@ def test_two_streams_each_with_its_workspace():
     for j in range(2):
         for i, y in enumerate(outs[j]):
             assert torch.equal(y, alone[j]), f"stream {j} call {i} differs"
+
+
+FWD_KEYS = {"x": "x", "dt": "dt", "z": "z", "B": "B_f", "C": "C_f", "A": "A_f", "D": "D_f", "dt_bias": "dt_bias_f"}
+
+
+@pytest.mark.parametrize("fill", ["random", "stale"])
+@pytest.mark.parametrize("B,L,Di,io,chunk", [(3, 300, 200, "f32", 20), (2, 197, 320, "bf16", 50), (2, 65, 32, "f32", 8)])
+def test_forward_only_workspace_contents_do_not_matter(B, L, Di, io, chunk, fill):
+    p = binding.launch_info(B, L, Di, 16, 0, io, chunk_len=chunk, forward_only=True)
+    assert 2 <= p["chunks"] <= 16 and p["kernels"] == 1
+    inp = make_inputs(B, L, Di, 16, io, seed=B * L + Di + 7)
+    dev = to_device(inp, io)
+    fargs = [dev[FWD_KEYS[k]] for k in FWD_KEYS]
+    need = binding.workspace_bytes(B, L, Di, 16, 0, io, chunk_len=chunk, forward_only=True)
+    fresh = binding.fwd(*fargs, chunk_len=chunk, workspace=torch.zeros(need, dtype=torch.uint8, device="cuda:0"))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    if fill == "random":
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(12)
+        ws.copy_(torch.randint(0, 256, (need,), generator=g, device="cuda:0", dtype=torch.int32).to(torch.uint8))
+    else:
+        other = to_device(make_inputs(B, L, Di, 16, io, seed=B * L + Di + 8), io)
+        binding.fwd(*[other[FWD_KEYS[k]] for k in FWD_KEYS], chunk_len=chunk, workspace=ws)
+    y = binding.fwd(*fargs, chunk_len=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, fresh), f"{fill} workspace changes the forward-only output"
+    ref = oracle.fwd({k: inp[v] for k, v in FWD_KEYS.items()})
+    assert_close(to_f64(y), ref, io, f"fwd chain B={B} L={L} Di={Di} {io} chunk={chunk} {fill}")

@@ -110,9 +110,9 @@ FOLD_MAX_CHUNKS = 16
 def test_chunk_counts_around_the_in_scan_fold(K, variant, io):
     """A sequence of up to FOLD_MAX_CHUNKS chunks runs without the carry-combine kernel: each scan
     workgroup folds the aggregates of the chunks before its own, four chunks per round of loads (one
-    round up to 5 chunks, several from 6); bidirectional, the aggregates are computed and handed
-    over inside the same kernel (one kernel per call); past that the aggregate pass and the
-    combine supply the entering states.
+    round up to 5 chunks, several from 6), the aggregates computed and handed over inside the same
+    kernel (one kernel per call); past that the aggregate pass and the combine supply the entering
+    states.
     Every variant against the oracle at each count, with a ragged last chunk and a ragged channel
     block, general transitions with fp32 io and geometric ones with bf16."""
     T, Di = 7, 96
@@ -121,6 +121,5 @@ def test_chunk_counts_around_the_in_scan_fold(K, variant, io):
     info = binding.launch_info(c["B"], c["L"], Di, 16, 0, io, chunk_len=T,
                                forward_only=variant in ("fwd", "fwd_swap"), aux_swap=variant == "fwd_swap")
     assert info["chunks"] == K
-    fwd = variant in ("fwd", "fwd_swap")
-    assert info["kernels"] == ((2 if fwd else 1) if K <= FOLD_MAX_CHUNKS else 3) + (1 if variant == "fwd_swap" else 0)
+    assert info["kernels"] == (1 if K <= FOLD_MAX_CHUNKS else 3) + (1 if variant == "fwd_swap" else 0)
     test_random_case_matches_oracle(c)
