@@ -149,7 +149,10 @@ def oracle_seconds(inp_np: dict, seg_len: int, runs: int = 3) -> float:
 def configs_leg(graph_wall, dev, steps, headline=None, with_cpu=True):
     """Every workload at its full size (tiny, Vim-Ti, Vim-S, high-res, folded), timed as HIP graph
     replays of the whole library call with the plan's own chunking, on inputs drawn on the device
-    with the same distributions; rotating input copies past the Infinity Cache (at most 64). The
+    with the same distributions; rotating input copies past the Infinity Cache (at most 64), timed
+    over whole graphs of back-to-back calls (at least two of them: max(steps, 2 x copies) calls,
+    rounded up to whole graphs), so that a small workload's time is its calls' and not the launch
+    of a one-call graph per step. The
     headline workload's entry is the headline measurement itself (headline = (name, seconds per
     step)), so the line holds one number for it. With with_cpu, the float64 oracle is timed on each
     workload's inputs (median of 3 runs on the host's cores)."""
@@ -173,10 +176,11 @@ def configs_leg(graph_wall, dev, steps, headline=None, with_cpu=True):
             outs = [torch.empty_like(inp["x"]) for _ in range(n)]
             params = [inp[k] for k in par_names]
             ws = torch.empty(max(plan["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+            nsteps = -(-max(steps, 2 * n) // n) * n
             wall = graph_wall(lambda i, s: binding.PreparedCall(*copies[i], *params, seg_len=w.seg_len, out=outs[i],
-                                                                workspace=ws, stream=s), ncopy=n)
-            step = wall / steps
-            source = f"HIP graph replays of the whole call, {n} rotating input copies"
+                                                                workspace=ws, stream=s), ncopy=n, steps=nsteps)
+            step = wall / nsteps
+            source = f"HIP graph replays of the whole call, {n} rotating input copies, {nsteps} calls"
             del copies, outs, ws
         ops = alu_ops_per_element(True) * w.tokens_channels
         res[w.name] = {"us_per_call": round(step * 1e6, 3), "gbs": round(nbytes / step / 1e9, 2),
@@ -465,11 +469,13 @@ def main(argv=None):
     wall, per_call, per_scan = timed(False)
     kernel_s = float(np.mean(per_scan))
     launch_mode = "eager library calls"
-    def graph_wall(make, ncopy=ncopy, warmup=None):
-        """Wall time of args.steps steps replayed from HIP graphs, each step the whole library call
-        (every kernel of the path) on input copy i % ncopy; make(i, stream) prepares that call on
-        the given stream. One graph holds ncopy consecutive steps, single-step graphs the rest."""
+    def graph_wall(make, ncopy=ncopy, warmup=None, steps=None):
+        """Wall time of `steps` (default args.steps) steps replayed from HIP graphs, each step the
+        whole library call (every kernel of the path) on input copy i % ncopy; make(i, stream)
+        prepares that call on the given stream. One graph holds ncopy consecutive steps,
+        single-step graphs the rest."""
         warmup = args.warmup if warmup is None else warmup
+        steps = args.steps if steps is None else steps
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -490,9 +496,9 @@ def main(argv=None):
             singles[i % ncopy].replay()
         torch.cuda.synchronize(dev)
         t0 = time.perf_counter()
-        for _ in range(args.steps // ncopy):
+        for _ in range(steps // ncopy):
             block.replay()
-        for i in range(args.steps % ncopy):
+        for i in range(steps % ncopy):
             singles[i].replay()
         torch.cuda.synchronize(dev)
         return time.perf_counter() - t0
