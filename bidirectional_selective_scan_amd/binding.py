@@ -50,7 +50,7 @@ class _Conv(ctypes.Structure):
 
 EXPORTED = ("vimscan_bidir_fwd", "vimscan_bidir_conv_fwd", "vimscan_fwd", "vimscan_plan_launch",
             "vimscan_workspace_bytes", "vimscan_status_string", "vimscan_version", "vimscan_ncssd_fwd",
-            "vimscan_ncssd_plan", "vimscan_bidir_order_fwd", "vimscan_bidir_fwd_noalloc")
+            "vimscan_ncssd_plan", "vimscan_bidir_order_fwd", "vimscan_bidir_fwd_noalloc", "vimscan_wait_timeouts")
 
 # Size of the static scratch array behind vimscan_bidir_fwd_noalloc (VIMSCAN_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 96 << 20
@@ -94,12 +94,23 @@ def load_library():
             lib.vimscan_ncssd_fwd.argtypes = [vp] * 4 + [ctypes.c_int64, vp, ctypes.POINTER(_Launch)]
             lib.vimscan_ncssd_plan.restype = ctypes.c_int
             lib.vimscan_ncssd_plan.argtypes = [ctypes.POINTER(_Launch), ctypes.c_int64, ctypes.POINTER(_Plan)]
+            lib.vimscan_wait_timeouts.restype = ctypes.c_int
+            lib.vimscan_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
             _lib = lib
     return _lib
 
 
 def status_string(status: int) -> str:
     return load_library().vimscan_status_string(int(status)).decode()
+
+
+def wait_timeouts() -> int:
+    """Waves of the one-kernel chunked scans on the current device whose wait for earlier chunks'
+    aggregates gave up after its bound since the library was loaded (vimscan_wait_timeouts; 0
+    unless the hardware broke the in-order dispatch the kernel relies on). Synchronous."""
+    n = ctypes.c_uint64(0)
+    _check(load_library().vimscan_wait_timeouts(ctypes.byref(n)))
+    return int(n.value)
 
 
 def _check(status: int):

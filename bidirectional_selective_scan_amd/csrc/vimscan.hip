@@ -1073,8 +1073,13 @@ __global__ __launch_bounds__(256) void k_chunk_aggregate(ScanArgs a) {
 // group not yet complete are the first ones waiting on their XCDs; with room for at least
 // kFoldMaxChunks workgroups per XCD (32 CUs, at least one workgroup each) all of them run at once
 // and complete, and so on group by group. The wait is bounded all the same (kSpinLimit reads,
-// about a second): past it the wave goes on, and its output is unspecified.
+// about a second): past it the wave goes on, its output is unspecified, and it counts itself in
+// g_wait_timeouts (vimscan_wait_timeouts).
 constexpr int kSpinLimit = 1 << 20;
+
+// Waits of the one-kernel chunked scans on this GPU that ran past kSpinLimit since the library was
+// loaded (none is expected: see the progress argument above).
+__device__ unsigned long long g_wait_timeouts;
 
 // llvm.amdgcn.dispatch.id: the dispatch packet's index in its queue, which the command processor
 // writes into two SGPRs of every wave it launches.
@@ -1105,11 +1110,14 @@ __device__ __forceinline__ void wait_published(const ScanArgs& a, const WgCoords
     const bool mine = c.lane < cnt;
     const int k = mine ? (c.dir == 0 ? c.lane : a.K - 1 - c.lane) : c.chunk;
     const uint64_t* w = tag_word(a, c.dir, c.seq, k, c.cb);
-    for (int it = 0; it < kSpinLimit; ++it) {
+    bool done = false;
+    for (int it = 0; it < kSpinLimit && !done; ++it) {
         const bool ready = !mine || __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-        if (__all(ready)) break;
-        __builtin_amdgcn_s_sleep(2);
+        done = __all(ready);
+        if (!done) __builtin_amdgcn_s_sleep(2);
     }
+    if (!done && c.lane == 0)
+        __hip_atomic_fetch_add(&g_wait_timeouts, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::: "memory");  // the aggregate loads stay after the wait
 }
 
@@ -1472,6 +1480,15 @@ int bidir_impl(const void* x, const void* dt, const void* z, const void* B_f, co
 }  // namespace
 
 extern "C" {
+
+int vimscan_wait_timeouts(uint64_t* count) {
+    if (!count) return VIMSCAN_ERR_NULL;
+    unsigned long long v = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_wait_timeouts), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return VIMSCAN_ERR_HIP;
+    *count = static_cast<uint64_t>(v);
+    return VIMSCAN_OK;
+}
 
 int vimscan_bidir_fwd(const void* x, const void* dt, const void* z, const void* B_f, const void* C_f,
                       const void* B_b, const void* C_b, const float* A_f, const float* A_b, const float* D_f,

@@ -296,6 +296,18 @@ const char* vimscan_status_string(int status);
 /* Library version string, e.g. "vimscan 0.3.0 gfx950". */
 const char* vimscan_version(void);
 
+/*
+ * Diagnostics of the one-kernel chunked scans (plans of 2..16 chunks): *count = the number of
+ * waves on the current HIP device, since the library was loaded, whose wait for the chunk
+ * aggregates of the earlier chunks of their sequence gave up after its bound (about a second);
+ * their calls' outputs are unspecified. The hardware starts the workgroups of every XCD in
+ * increasing id order, which makes every such wait end (the kernel's own comment gives the
+ * argument), so the count stays 0; it exists so that a failure of that premise is visible.
+ * Synchronous (a device-to-host copy after the device's queued work). Returns VIMSCAN_OK,
+ * VIMSCAN_ERR_NULL or VIMSCAN_ERR_HIP.
+ */
+int vimscan_wait_timeouts(uint64_t* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,10 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(binding.EXPORTED)
 
 
+def test_wait_timeouts_rejects_null_before_any_hip_call(lib):
+    assert lib.vimscan_wait_timeouts(None) == NULL
+
+
 def test_status_strings(lib):
     for code in range(0, -13, -1):
         s = binding.status_string(code)

@@ -12,7 +12,9 @@ What these tests pin down beyond the plain parity tests:
 * the plan: one kernel per call, a tag word per (direction, sequence, chunk, channel block) in the
   workspace after the other regions;
 * the same for the forward-only scan (vimscan_fwd), whose chunked plans of up to 16 chunks are one
-  kernel as well.
+  kernel as well;
+* no wait of any of these calls (or of any earlier test in the process) gave up after its bound
+  (vimscan_wait_timeouts stays 0).
 Shapes: ragged last chunks, a ragged last channel block and an odd channel-block count (a spare
 wave that neither publishes nor waits), 2 to 16 chunks, fp32 and bf16 io."""
 import numpy as np
@@ -143,3 +145,11 @@ def test_forward_only_workspace_contents_do_not_matter(B, L, Di, io, chunk, fill
     assert torch.equal(y, fresh), f"{fill} workspace changes the forward-only output"
     ref = oracle.fwd({k: inp[v] for k, v in FWD_KEYS.items()})
     assert_close(to_f64(y), ref, io, f"fwd chain B={B} L={L} Di={Di} {io} chunk={chunk} {fill}")
+
+
+def test_no_wait_gave_up():
+    """Runs after the calls above in this file (and whatever ran before in the process)."""
+    dev = to_device(make_inputs(3, 300, 200, 16, "f32", seed=5), "f32")
+    binding.bidir_fwd(*_args(dev), chunk_len=20)
+    torch.cuda.synchronize()
+    assert binding.wait_timeouts() == 0
