@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 FP32_VECTOR_TFLOPS = 157.3    # MI355X fp32 vector peak, published: packed FMA, 256 CU x 128 lanes x 2 x 2.4 GHz
-# Issue peak of the fp32 VALU without packed instructions (this build compiles them out): each of
+# Issue peak of the fp32 VALU without packed instructions (the library is compiled without them): each of
 # the 4 SIMDs of a CU issues one wave64 instruction per 4 cycles, 16 lanes a cycle, so
 # 256 CU x 64 lanes x 2.4 GHz lane-operations per second.
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
@@ -322,7 +322,7 @@ def main(argv=None):
                     help="only copy a MIB-mebibyte buffer 5 times (a known-size kernel for HBM counter scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the scan on a single MI355X and has no "
+        print("bench.py measures one GPU: the library runs the scan on a single MI355X and has no "
               "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
