@@ -76,8 +76,10 @@ enum vimscan_io_dtype { VIMSCAN_F32 = 0, VIMSCAN_BF16 = 1 };
 
 /* flags */
 /* Evaluate exp(delta*A[d,n]) once per (token, channel, state) even when a channel's A row is
-   an arithmetic progression in n, for which the library otherwise forms the transitions as
-   exp(delta*A[d,0]) * exp(delta*(A[d,1]-A[d,0]))^n. Both give the defined result. */
+   an arithmetic progression in n that is non-positive and non-increasing (A[d,0] <= 0 and
+   A[d,1] - A[d,0] <= 0), for which the library otherwise forms the transitions as
+   exp(delta*A[d,0]) * exp(delta*(A[d,1]-A[d,0]))^n. Both give the defined result. Other rows
+   always take one exponential per state. */
 #define VIMSCAN_FLAG_GENERAL_DECAY 1
 /* Auxiliary-token swap (SF-Mamba page, "auxiliary patch swapping"): after the scan, exchange
    the outputs of the first and the last token of every sequence (every segment when
