@@ -144,12 +144,11 @@ typedef struct vimscan_plan {
     int64_t chunk_len;      /* tokens per chunk */
     int64_t chunks;         /* chunks per sequence; 1 = single pass (no chunk carries) */
     int64_t workgroups;     /* workgroups of the main scan kernel */
-    int32_t kernels;        /* kernels launched per call: 1 for a single pass and, in both
-                               directions, for 2..16 chunks per sequence (one kernel computes
-                               each chunk's aggregate, hands it to the later chunks through the
-                               workspace and folds those it receives); past 16 chunks 3 (chunk
-                               aggregates, carry combine, scan); forward only 2 for 2..16 chunks
-                               (aggregates, scan folding them); plus 1 with
+    int32_t kernels;        /* kernels launched per call: 1 for a single pass and for 2..16
+                               chunks per sequence (one kernel computes each chunk's aggregate,
+                               hands it to the later chunks through the workspace and folds
+                               those it receives), bidirectional and forward only alike; past
+                               16 chunks 3 (chunk aggregates, carry combine, scan); plus 1 with
                                VIMSCAN_FLAG_AUX_SWAP */
     int32_t park_in_workspace; /* 1: the two directions exchange their outputs through the
                                workspace (long chunks); 0: through LDS */
