@@ -11,8 +11,9 @@
 //  * Folding: with a reset every seg_len tokens, the segments are independent sequences; in the
 //    dense [batch][seqlen][.] layout a folded stream of B*T tokens is byte-for-byte the layout of
 //    B sequences of T tokens, so the kernels index segments as sequences. No copy, no select.
-//  * One workgroup = one chunk of one sequence x 64 channels, two waves: wave 0 runs the forward
-//    recurrence, wave 1 the backward one, one channel per lane, the 16 states in VGPRs. A token's
+//  * One workgroup = one chunk of one sequence x one or two blocks of 64 channels, two waves per
+//    block: one runs the forward recurrence, the other the backward one, one channel per lane, the
+//    16 states in VGPRs (forward only: every wave is a block of its own). A token's
 //    B and C rows are the same for every channel of a sequence, so they are wave-uniform: the
 //    chunk's B and C rows of both directions are staged once per workgroup in LDS as fp32
 //    (bf16 widened on the way) and read as broadcasts. Nothing in the token loop goes through
@@ -31,9 +32,10 @@
 //    chunk and direction the local end state from zero and the sum of delta over the chunk (the
 //    chunk's transition product is exp(A * sum delta)) -- the chunk aggregate; folded in scan
 //    order they give the state entering every chunk, from which the chunk is scanned with the
-//    readout. Up to kFoldMaxChunks chunks per sequence (bidirectional) this is one kernel: each
-//    workgroup computes its own chunk's aggregates, hands them to the other chunks of its
-//    sequence through the workspace (k_bidir_chain, k_fwd_chain) and folds the ones it receives.
+//    readout. Up to kFoldMaxChunks chunks per sequence (both directions or forward only) this is
+//    one kernel: each workgroup computes its own chunk's aggregates, hands them to the other
+//    chunks of its sequence through the workspace (k_bidir_chain, k_fwd_chain) and folds the
+//    ones it receives.
 //    Beyond that an aggregate pass, a combine kernel and the scan run as separate kernels.
 //    Carries live in the caller's workspace.
 //  * delta is kept in log2 units (softplus * log2 e), so the transitions are the hardware exp2
@@ -41,8 +43,9 @@
 //    as C * ln 2). When a channel's A row is an arithmetic progression in n, the 16 transitions
 //    are exp(delta*A0) * q^n with q = exp(delta*dA): two exponentials (one when A0 == dA, as in
 //    the S4D-real initialisation A[d,n] = -(n+1)) and multiplies instead of 16 exponentials
-//    (the transcendental unit issues at a quarter of the FMA rate). A wave takes that path
-//    only when every lane's row qualifies; VIMSCAN_FLAG_GENERAL_DECAY turns it off.
+//    (an exponential takes two VALU issue slots, an FMA one). A wave takes that path only when
+//    every lane's row qualifies (an exact progression with A0 <= 0 and dA <= 0);
+//    VIMSCAN_FLAG_GENERAL_DECAY turns it off.
 //  * Workgroup ids are remapped so that consecutive logical workgroups (which share a
 //    sequence's B/C rows) land on the same XCD and its L2.
 //  * Variants of the same kernels (a template parameter): the directional convolution in front
